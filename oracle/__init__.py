@@ -1,0 +1,44 @@
+"""fp64 CPU reference for tiled attention with an online softmax (test infrastructure).
+
+This package is the oracle that the GPU library is checked against. It is test
+infrastructure, not part of the product: only ``tests/``, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import it. It
+shares no code with the HIP library or its Python binding and imports neither.
+
+What it computes is the plain definition of attention given in "Why your local
+LLM feels dumber than it is" (section "What attention is trying to calculate"):
+score = scale * dot(query, key), weight = exp(score), normalized over the keys a
+query may see, output = weighted sum of values. The tiled, online-softmax GPU
+method ("Streaming process", steps 3-8 and its code snippet) reaches the same
+result up to rounding order, so the oracle is that definition written out, in
+float64, on the exact upcasts of the bits the GPU receives.
+
+Forms:
+- ``attention_dense`` / ``decode_dense``: materialized scores per (sequence,
+  head), the naive form of "GPU Datapath", section C, harmless on a CPU.
+- ``attention_brute`` / ``decode_brute``: pure-Python loops with ``math.fsum``
+  for tiny inputs and the worked example.
+- ``decode_split_partials`` + ``combine_partials``: the split-into-groups form
+  of "Why the calculation is split into groups" with the log-sum-exp merge of
+  the FlashAttention 2 style described under "Backend names expand into four
+  decode algorithms"; also the combine oracle for arbitrary partials.
+- ``emulate``: fp32/bf16 scalar emulation used only to pin the split geometry
+  and merge formula against the numbers printed under "Plugging in actual
+  numbers".
+
+Every function is pinned by ``tests/test_oracle_*.py`` against values printed
+on the pages (``tests/golden/``), closed forms, special cases, brute force and
+invariances. Readings of points the pages leave open are listed in the
+project's design notes.
+"""
+from .reference import (  # noqa: F401
+    attention_dense,
+    attention_brute,
+    decode_dense,
+    decode_brute,
+    gather_sequence_kv,
+    page_split_ranges,
+    decode_split_partials,
+    combine_partials,
+)
+from . import emulate  # noqa: F401

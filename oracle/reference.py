@@ -1,0 +1,236 @@
+"""fp64 attention reference (test infrastructure; see the package docstring).
+
+Notation (from "Why your local LLM feels dumber than it is", section "What
+attention is trying to calculate", and the FlashAttention loop of "Streaming
+process", code snippet): for query row i of head h and admissible keys J(i),
+    s_ij = scale * sum_d q[i,h,d] * k[j,g,d]
+    m_i  = max_{j in J(i)} s_ij
+    w_ij = exp(s_ij - m_i)
+    l_i  = sum_{j in J(i)} w_ij
+    O[i,h,:] = sum_j w_ij * v[j,g,:] / l_i
+    LSE[i,h] = m_i + ln l_i            (natural log, scaled-score units)
+Subtracting m_i changes nothing in exact arithmetic (section "Why the
+calculation is split into groups"); it only keeps exp finite.
+Readings where the pages are silent:
+- GQA: query head h uses key/value head g = h // (Hq / Hkv) (contiguous groups).
+- causal: key j is admissible for query i when j <= i, positions counted from
+  the start of each sequence (Sq = Sk per sequence).
+- decode: the one query token sees every cached token, seq_lens[b] of them.
+- an empty key set gives O = 0 and LSE = -inf.
+Inputs are float64 arrays (exact upcasts of bf16/fp32 storage).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = float("-inf")
+
+
+def _softmax_rows(S: np.ndarray, V: np.ndarray):
+    """Return (O, LSE) for score rows S [n, L] (with -inf for inadmissible
+    keys) against values V [L, D]. Rows with no admissible key give (0, -inf)."""
+    n = S.shape[0]
+    D = V.shape[1]
+    O = np.zeros((n, D), dtype=np.float64)
+    lse = np.full(n, NEG_INF, dtype=np.float64)
+    if n == 0 or S.shape[1] == 0:
+        return O, lse
+    m = S.max(axis=1)
+    ok = np.isfinite(m)
+    if not ok.any():
+        return O, lse
+    Sm = S[ok]
+    mm = m[ok]
+    W = np.exp(Sm - mm[:, None])          # exp(-inf) = 0 for masked keys
+    l = W.sum(axis=1)
+    O[ok] = (W @ V) / l[:, None]
+    lse[ok] = mm + np.log(l)
+    return O, lse
+
+
+def attention_dense(q, k, v, cu_seqlens, num_q_heads: int, num_kv_heads: int,
+                    scale: float, causal: bool):
+    """Materialized attention over packed variable-length sequences.
+
+    q [T, Hq, D], k/v [T, Hkv, D] float64; cu_seqlens int [n+1].
+    Returns O [T, Hq, D] float64 and LSE [Hq, T] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, Hq, D = q.shape
+    assert Hq == num_q_heads and k.shape[1] == num_kv_heads
+    assert num_q_heads % num_kv_heads == 0
+    group = num_q_heads // num_kv_heads
+    O = np.zeros((T, Hq, v.shape[2]), dtype=np.float64)
+    LSE = np.full((Hq, T), NEG_INF, dtype=np.float64)
+    cu = [int(x) for x in cu_seqlens]
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        L = s1 - s0
+        if L <= 0:
+            continue
+        mask = np.triu(np.ones((L, L), dtype=bool), 1) if causal else None
+        for h in range(Hq):
+            g = h // group
+            S = scale * (q[s0:s1, h, :] @ k[s0:s1, g, :].T)
+            if mask is not None:
+                S[mask] = NEG_INF
+            o, l = _softmax_rows(S, v[s0:s1, g, :])
+            O[s0:s1, h] = o
+            LSE[h, s0:s1] = l
+    return O, LSE
+
+
+def attention_brute(q, k, v, cu_seqlens, num_q_heads: int, num_kv_heads: int,
+                    scale: float, causal: bool):
+    """The same definition with scalar Python loops and exactly rounded sums
+    (math.fsum); meant for a few dozen rows. Returns lists shaped like
+    attention_dense's outputs (as float64 arrays)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    T, Hq, D = q.shape
+    group = num_q_heads // num_kv_heads
+    O = np.zeros((T, Hq, v.shape[2]))
+    LSE = np.full((Hq, T), NEG_INF)
+    cu = [int(x) for x in cu_seqlens]
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        for h in range(Hq):
+            g = h // group
+            for i in range(s0, s1):
+                keys = range(s0, i + 1) if causal else range(s0, s1)
+                scores = [scale * math.fsum(float(q[i, h, d]) * float(k[j, g, d]) for d in range(D))
+                          for j in keys]
+                if not scores:
+                    continue
+                m = max(scores)
+                w = [math.exp(s - m) for s in scores]
+                l = math.fsum(w)
+                for d in range(v.shape[2]):
+                    O[i, h, d] = math.fsum(wj * float(v[j, g, d]) for wj, j in zip(w, keys)) / l
+                LSE[h, i] = m + math.log(l)
+    return O, LSE
+
+
+# --------------------------------------------------------------------------
+# paged decode ("GPU Datapath", section D: one query token per sequence, the
+# KV cache read through a block table of 16-token pages)
+# --------------------------------------------------------------------------
+def gather_sequence_kv(k_cache, v_cache, block_table, seq_len: int, b: int):
+    """Logical token t of sequence b sits in physical page block_table[b, t//P],
+    slot t % P. Returns K, V [seq_len, Hkv, D] for that sequence."""
+    P = k_cache.shape[1]
+    n_pages = (seq_len + P - 1) // P
+    pages = [int(x) for x in block_table[b, :n_pages]]
+    if n_pages == 0:
+        shp = (0,) + tuple(k_cache.shape[2:])
+        return np.zeros(shp), np.zeros(shp)
+    K = np.concatenate([k_cache[p] for p in pages], axis=0)[:seq_len]
+    V = np.concatenate([v_cache[p] for p in pages], axis=0)[:seq_len]
+    return np.asarray(K, dtype=np.float64), np.asarray(V, dtype=np.float64)
+
+
+def decode_dense(q, k_cache, v_cache, block_table, seq_lens, scale: float):
+    """q [B, Hq, D]; caches [pages, P, Hkv, D]; returns O [B, Hq, D], LSE [B, Hq]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    Hkv = k_cache.shape[2]
+    group = Hq // Hkv
+    O = np.zeros((B, Hq, v_cache.shape[3]))
+    LSE = np.full((B, Hq), NEG_INF)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        K, V = gather_sequence_kv(k_cache, v_cache, block_table, L, b)
+        for h in range(Hq):
+            g = h // group
+            S = (scale * (K[:, g, :] @ q[b, h, :]))[None, :]
+            o, l = _softmax_rows(S, V[:, g, :])
+            O[b, h] = o[0]
+            LSE[b, h] = l[0]
+    return O, LSE
+
+
+def decode_brute(scores, values):
+    """Exact scalar softmax-weighted mean for one query: the max-subtracted,
+    exactly rounded form (section "Plugging in actual numbers" gives this
+    shape of reference). scores, values: 1-D sequences. Returns (o, lse)."""
+    scores = [float(s) for s in scores]
+    if not scores:
+        return 0.0, NEG_INF
+    m = max(scores)
+    w = [math.exp(s - m) for s in scores]
+    l = math.fsum(w)
+    return math.fsum(wi * float(vi) for wi, vi in zip(w, values)) / l, m + math.log(l)
+
+
+# --------------------------------------------------------------------------
+# split-KV partials and their log-sum-exp merge
+# ("Why the calculation is split into groups"; the FlashAttention 2 merge of
+#  normalized fp32 partial outputs weighted by exp(LSE_s - max LSE) described
+#  under "Backend names expand into four decode algorithms")
+# --------------------------------------------------------------------------
+def page_split_ranges(n_pages: int, num_splits: int):
+    """Contiguous, page-aligned groups with equal page counts
+    ceil(n_pages / num_splits); trailing groups may be empty."""
+    if num_splits < 1:
+        raise ValueError("num_splits must be >= 1")
+    pps = -(-n_pages // num_splits) if n_pages > 0 else 0
+    return [(min(s * pps, n_pages), min((s + 1) * pps, n_pages)) for s in range(num_splits)]
+
+
+def decode_split_partials(q, k_cache, v_cache, block_table, seq_lens, scale: float,
+                          num_splits: int):
+    """Per (sequence, q-head, split): the normalized partial output
+    O_s = sum w v / l over the split's keys and LSE_s = m_s + ln l_s, with
+    (0, -inf) for an empty split. Returns po [B*Hq, S, D], plse [B*Hq, S]."""
+    q = np.asarray(q, dtype=np.float64)
+    B, Hq, D = q.shape
+    P = k_cache.shape[1]
+    Hkv = k_cache.shape[2]
+    group = Hq // Hkv
+    po = np.zeros((B * Hq, num_splits, v_cache.shape[3]))
+    plse = np.full((B * Hq, num_splits), NEG_INF)
+    for b in range(B):
+        L = int(seq_lens[b])
+        if L <= 0:
+            continue
+        K, V = gather_sequence_kv(k_cache, v_cache, block_table, L, b)
+        n_pages = (L + P - 1) // P
+        for s, (p0, p1) in enumerate(page_split_ranges(n_pages, num_splits)):
+            t0, t1 = p0 * P, min(p1 * P, L)
+            if t1 <= t0:
+                continue
+            for h in range(Hq):
+                g = h // group
+                S = (scale * (K[t0:t1, g, :] @ q[b, h, :]))[None, :]
+                o, l = _softmax_rows(S, V[t0:t1, g, :])
+                po[b * Hq + h, s] = o[0]
+                plse[b * Hq + h, s] = l[0]
+    return po, plse
+
+
+def combine_partials(po, plse):
+    """Merge split partials: M = max over non-empty splits of LSE_s,
+    w_s = exp(LSE_s - M), O = sum_s w_s O_s / sum_s w_s, LSE = M + ln sum_s w_s.
+    A row whose splits are all empty gives (0, -inf).
+    po [rows, S, D], plse [rows, S] -> O [rows, D], LSE [rows]."""
+    po = np.asarray(po, dtype=np.float64)
+    plse = np.asarray(plse, dtype=np.float64)
+    rows, S, D = po.shape
+    O = np.zeros((rows, D))
+    LSE = np.full(rows, NEG_INF)
+    for r in range(rows):
+        ne = np.isfinite(plse[r])
+        if not ne.any():
+            continue
+        M = plse[r, ne].max()
+        w = np.exp(plse[r, ne] - M)
+        W = w.sum()
+        O[r] = (w[:, None] * po[r, ne]).sum(axis=0) / W
+        LSE[r] = M + math.log(W)
+    return O, LSE
