@@ -1,0 +1,93 @@
+// Log-sum-exp merge of split partials ("Why your local LLM feels dumber than
+// it is", section "Backend names expand into four decode algorithms",
+// FlashAttention 2 entry: fp32 normalised partial outputs weighted by
+// exp(LSE_s - max LSE)).
+//
+// One workgroup of 256 threads per output row. Each thread owns four
+// consecutive output columns and a residue class of splits; partial sums are
+// folded through LDS in a fixed order, so the result does not depend on
+// scheduling. Empty splits (LSE = -inf) are skipped; an all-empty row gives
+// O = 0 and LSE = -inf.
+#pragma once
+#include "common.h"
+
+namespace miattn {
+
+struct CombineArgs {
+  const float* part_o;    // [rows, S, D]
+  const float* part_lse;  // [rows, S]
+  void* o;                // [rows, D] bf16 or fp32
+  float* lse;             // [rows] or null
+  int rows;
+  int num_splits;
+  int head_dim;
+  int out_bf16;
+};
+
+__device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
+  const int t = threadIdx.x;
+  red[t] = v;
+  __syncthreads();
+#pragma unroll
+  for (int s = 128; s > 0; s >>= 1) {
+    if (t < s) red[t] = is_max ? fmaxf(red[t], red[t + s]) : red[t] + red[t + s];
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(256) void miattn_combine_kernel(CombineArgs a) {
+  __shared__ float red[256];
+  __shared__ f32x4 part[256];
+  const int row = blockIdx.x;
+  const int S = a.num_splits;
+  const int D = a.head_dim;
+  const int DQ = D / 4;
+  const int NG = 256 / DQ;
+  const int t = threadIdx.x;
+  const float* pl = a.part_lse + (size_t)row * S;
+  const float* po = a.part_o + (size_t)row * S * D;
+
+  float mx = kNegInf;
+  for (int s = t; s < S; s += 256) mx = fmaxf(mx, pl[s]);
+  const float M = block_reduce(mx, red, true);
+  const bool empty = (M == kNegInf);
+  float ws = 0.f;
+  if (!empty)
+    for (int s = t; s < S; s += 256) {
+      const float x = pl[s];
+      ws += (x == kNegInf) ? 0.f : exp2_hw((x - M) * kLog2e);
+    }
+  const float W = block_reduce(ws, red, false);
+
+  const int c = t % DQ;
+  const int gi = t / DQ;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (!empty && gi < NG) {
+    for (int s = gi; s < S; s += NG) {
+      const float x = pl[s];
+      if (x == kNegInf) continue;
+      const float w = exp2_hw((x - M) * kLog2e);
+      acc += w * *reinterpret_cast<const f32x4*>(po + (size_t)s * D + 4 * c);
+    }
+  }
+  part[t] = acc;
+  __syncthreads();
+  if (gi == 0) {
+    f32x4 sum = part[c];
+    for (int k = 1; k < NG; ++k) sum += part[k * DQ + c];
+    const float inv = empty ? 0.f : 1.f / W;
+    sum *= inv;
+    if (a.out_bf16) {
+      u32x2 w2 = {pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+      *reinterpret_cast<u32x2*>((uint16_t*)a.o + (size_t)row * D + 4 * c) = w2;
+    } else {
+      *reinterpret_cast<f32x4*>((float*)a.o + (size_t)row * D + 4 * c) = sum;
+    }
+    if (a.lse != nullptr && c == 0) a.lse[row] = empty ? kNegInf : M + log2_hw(W) * kLn2;
+  }
+}
+
+}  // namespace miattn

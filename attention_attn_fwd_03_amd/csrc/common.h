@@ -1,0 +1,80 @@
+// Device-side building blocks shared by the gfx950 attention kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 f16x4_lds __attribute__((__vector_size__(4 * sizeof(__fp16))));
+
+#define MIATTN_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// v_exp_f32 / v_log_f32: base-2 transcendental unit.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// Two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// Value held by lane (lane ^ 32): v_permlane32_swap exchanges the upper half
+// wave's first operand with the lower half's second; passing x twice gives
+// each lane its partner's copy in the element it did not keep.
+__device__ __forceinline__ float xor32(float x) {
+  int xi = __builtin_bit_cast(int, x);
+  auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  return __builtin_bit_cast(float, lane < 32 ? (int)r[1] : (int)r[0]);
+}
+
+// Value held by lane (lane ^ 16): ds_swizzle in bit-mask mode with xor mask 16.
+__device__ __forceinline__ float xor16(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, x), 0x401F));
+}
+
+__device__ __forceinline__ int lane_id() {
+  return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// 16-byte global load / store through plain vector types.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x4 lds_ld16(const MIATTN_LDS void* p) {
+  return *reinterpret_cast<const MIATTN_LDS u32x4*>(p);
+}
+__device__ __forceinline__ void lds_st16(MIATTN_LDS void* p, u32x4 v) {
+  *reinterpret_cast<MIATTN_LDS u32x4*>(p) = v;
+}
+
+// ds_read_b64_tr_b16. Within each block of 16 lanes, lane k names 4 consecutive
+// 16-bit elements (row k/4, columns 4(k%4)..4(k%4)+3 of a 4 x 16 tile when the
+// addresses are laid out that way); lane j receives column j of the 4 rows.
+__device__ __forceinline__ u32x2 lds_ld_tr16(const MIATTN_LDS void* p) {
+  f16x4_lds v = __builtin_amdgcn_ds_read_tr16_b64_v4f16((MIATTN_LDS f16x4_lds*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x2 a, u32x2 b) {
+  u32x4 v = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+__device__ __forceinline__ bf16x4 as_bf16x4(u32x2 v) { return __builtin_bit_cast(bf16x4, v); }
+
+}  // namespace miattn

@@ -1,0 +1,246 @@
+// Paged split-KV decode on gfx950.
+//
+// One query token per sequence reads its KV cache through a block table of
+// 16-token pages ("GPU Datapath: Where Every Byte Moves", section D). The
+// cached context is cut into contiguous page-aligned groups; each group
+// produces a normalised partial output and its log-sum-exp ("Why your local
+// LLM feels dumber than it is", section "Why the calculation is split into
+// groups"), merged afterwards by the combine kernel.
+//
+// Work decomposition: one workgroup of 4 waves per (split, kv head, sequence).
+// The G = Hq/Hkv query heads that share a kv head are served together, so each
+// K/V byte is read from HBM once. Inside the split, wave w takes pages w, w+4,
+// ..., keeps its own running max / sum / output, and the four waves are merged
+// through LDS in a fixed order at the end.
+//
+// Per page (16 tokens) a wave computes S^T = K . Q^T with 16x16x32 bf16 MFMAs
+// (rows: tokens, columns: query heads, padded to 16), so lane l holds query
+// head l%16 for tokens 4(l/16)..4(l/16)+3. Those four probabilities, rounded
+// to bf16, are directly the B operand of a 16x16x16 MFMA computing
+// O^T += V^T . P^T; the V^T operand comes from the page staged in LDS and read
+// back with the transposing ds_read_b64_tr_b16.
+#pragma once
+#include "common.h"
+
+namespace miattn {
+
+struct DecodeArgs {
+  const uint16_t* q;            // [B, Hq, D] bf16
+  const uint16_t* k_cache;      // [num_pages, 16, Hkv, D] bf16
+  const uint16_t* v_cache;
+  const int32_t* block_table;   // [B, max_pages]
+  const int32_t* seq_lens;      // [B]
+  float* part_o;                // [B*Hq, S, D] fp32   (num_splits > 1)
+  float* part_lse;              // [B*Hq, S] fp32
+  uint16_t* o;                  // [B, Hq, D] bf16     (num_splits == 1)
+  float* lse;                   // [B, Hq] fp32 or null
+  int max_pages;
+  int num_pages;
+  int num_q_heads;
+  int num_kv_heads;
+  int group;                    // G = Hq / Hkv (<= 8)
+  int num_splits;
+  float c;                      // scale * log2(e)
+};
+
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeMaxGroup = 8;
+constexpr int kPage = 16;
+// Lazy rescaling: the running max only moves when a page's max exceeds it by
+// more than this many powers of two, so the stored probabilities stay <= 2^8.
+constexpr float kRescaleThreshold = 8.0f;
+
+template <int D>
+struct DecodeSmem {
+  static constexpr int kRowElems = D + 8;                         // padded V row (bf16)
+  static constexpr int kStageBytes = kDecodeWaves * kPage * kRowElems * 2;
+  static constexpr int kMergeBytes = kDecodeWaves * kDecodeMaxGroup * D * 4;
+  static constexpr int kBytes = (kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes)
+                                + 2 * kDecodeWaves * 16 * 4;      // m and l per wave and head
+};
+
+template <int D>
+__global__ __launch_bounds__(256) void miattn_decode_split_kernel(DecodeArgs a) {
+  constexpr int NKK = D / 32;   // 16x16x32 steps over the head dim, one 16-B chunk each
+  constexpr int NDT = D / 16;   // 16-wide d tiles of the output
+  using Smem = DecodeSmem<D>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Smem::kBytes];
+
+  const int split = blockIdx.x;
+  const int g = blockIdx.y;
+  const int b = blockIdx.z;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int tok = lane & 15;     // token row for K/V loads and the S^T A operand
+  const int quad = lane >> 4;    // 0..3
+  const int hl = lane & 15;      // query head (within the group) owned by this lane
+  const int G = a.group;
+  const int Hkv = a.num_kv_heads;
+
+  int L = a.seq_lens[b];
+  L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
+  const int n_pages = (L + kPage - 1) / kPage;
+  const int pps = (n_pages + a.num_splits - 1) / a.num_splits;
+  const int p0 = split * pps < n_pages ? split * pps : n_pages;
+  const int p1 = p0 + pps < n_pages ? p0 + pps : n_pages;
+  // pages p0 + wave + 4*i, i < np
+  const int np = (p1 - p0 - wave + kDecodeWaves - 1) / kDecodeWaves > 0
+                     ? (p1 - p0 - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
+
+  // Q^T operand: head hl, d = 32*kk + 8*quad .. +7 (zero for padding heads).
+  u32x4 qop[NKK];
+  {
+    const bool live = hl < G;
+    const uint16_t* qp = a.q + ((size_t)b * a.num_q_heads + (size_t)g * G + (live ? hl : 0)) * D + 8 * quad;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qop[kk] = live ? ld16(qp + 32 * kk) : z;
+    }
+  }
+
+  const size_t row_stride = (size_t)Hkv * D;               // elements between tokens
+  const size_t page_stride = (size_t)kPage * row_stride;   // elements between pages
+  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+
+  float m = kNegInf;   // running max (log2 units) for head hl
+  float l = 0.f;       // partial running sum over this lane's tokens
+  f32x4 acc[NDT];
+#pragma unroll
+  for (int i = 0; i < NDT; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+  MIATTN_LDS uint16_t* vstage = (MIATTN_LDS uint16_t*)(smem) + wave * kPage * Smem::kRowElems;
+
+  // Physical page of the wave's i-th page, or -1 when out of range.
+  auto phys_page = [&](int i) -> int {
+    int pp = bt[p0 + wave + kDecodeWaves * i];
+    return (pp >= 0 && pp < a.num_pages) ? pp : -1;
+  };
+  // Token slot `tok` of logical page lp is a real token?
+  auto load_page = [&](int i, u32x4* kb, u32x4* vb) {
+    const int lp = p0 + wave + kDecodeWaves * i;
+    const int pp = phys_page(i);
+    const bool ok = pp >= 0 && lp * kPage + tok < L;
+    const uint16_t* kp = a.k_cache + (size_t)(ok ? pp : 0) * page_stride + (size_t)tok * row_stride
+                         + (size_t)g * D + 8 * quad;
+    const uint16_t* vp = a.v_cache + (kp - a.k_cache);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      kb[kk] = ok ? ld16(kp + 32 * kk) : z;
+      vb[kk] = ok ? ld16(vp + 32 * kk) : z;
+    }
+  };
+
+  auto process = [&](int i, const u32x4* kb, const u32x4* vb) {
+    const int lp = p0 + wave + kDecodeWaves * i;
+    const bool page_ok = phys_page(i) >= 0;
+    // S^T = K . Q^T  (16 tokens x 16 heads)
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[kk]), as_bf16x8(qop[kk]), s, 0, 0, 0);
+    // stage V for the transposing reads (tokens x d, padded rows)
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      lds_st16(vstage + tok * Smem::kRowElems + 32 * kk + 8 * quad, vb[kk]);
+    float t[4];
+    float pm = kNegInf;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tk = lp * kPage + 4 * quad + r;
+      t[r] = (page_ok && tk < L) ? s[r] * a.c : kNegInf;
+      pm = fmaxf(pm, t[r]);
+    }
+    pm = fmaxf(pm, xor16(pm));
+    pm = fmaxf(pm, xor32(pm));
+    if (__builtin_amdgcn_ballot_w64(pm > m + kRescaleThreshold)) {
+      const float mn = fmaxf(m, pm);
+      const float alpha = (m == kNegInf) ? 0.f : exp2_hw(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+      m = mn;
+    }
+    const float mu = (m == kNegInf) ? 0.f : m;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = exp2_hw(t[r] - mu);
+    l += (p[0] + p[1]) + (p[2] + p[3]);
+    u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    const bf16x4 pop = as_bf16x4(pw);
+    // O^T += V^T . P^T, one 16x16x16 MFMA per 16-wide d tile
+    const MIATTN_LDS uint16_t* vt = vstage + (4 * quad + (tok >> 2)) * Smem::kRowElems + 4 * (tok & 3);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const bf16x4 vop = as_bf16x4(lds_ld_tr16(vt + 16 * dt));
+      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, acc[dt], 0, 0, 0);
+    }
+  };
+
+  {
+    u32x4 kb0[NKK], vb0[NKK], kb1[NKK], vb1[NKK];
+    if (np > 0) load_page(0, kb0, vb0);
+    if (np > 1) load_page(1, kb1, vb1);
+    for (int i = 0; i < np; i += 2) {
+      process(i, kb0, vb0);
+      if (i + 2 < np) load_page(i + 2, kb0, vb0);
+      if (i + 1 < np) {
+        process(i + 1, kb1, vb1);
+        if (i + 3 < np) load_page(i + 3, kb1, vb1);
+      }
+    }
+  }
+
+  // full per-head sum over the four token quads of the wave
+  l += xor16(l);
+  l += xor32(l);
+
+  __syncthreads();   // staging area is reused for the merge below
+  float* mo = (float*)smem;                                                // [wave][G][D]
+  float* mm = (float*)(smem + (Smem::kBytes - 2 * kDecodeWaves * 16 * 4)); // [wave][16]
+  float* ml = mm + kDecodeWaves * 16;                                      // [wave][16]
+  if (quad == 0) {
+    mm[wave * 16 + hl] = m;
+    ml[wave * 16 + hl] = l;
+  }
+  if (hl < G) {
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+      *reinterpret_cast<f32x4*>(mo + ((size_t)wave * G + hl) * D + 16 * dt + 4 * quad) = acc[dt];
+  }
+  __syncthreads();
+
+  const int S = a.num_splits;
+  for (int idx = threadIdx.x; idx < G * (D / 4); idx += 256) {
+    const int h = idx / (D / 4);
+    const int d4 = (idx % (D / 4)) * 4;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, mm[w * 16 + h]);
+    float Lsum = 0.f;
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < kDecodeWaves; ++w) {
+      const float mw = mm[w * 16 + h];
+      const float f = (mw == kNegInf) ? 0.f : exp2_hw(mw - M);
+      Lsum += f * ml[w * 16 + h];
+      o += f * *reinterpret_cast<const f32x4*>(mo + ((size_t)w * G + h) * D + d4);
+    }
+    const bool empty = !(Lsum > 0.f);
+    const float inv = empty ? 0.f : 1.f / Lsum;
+    o *= inv;
+    const float lse = empty ? kNegInf : (M + log2_hw(Lsum)) * kLn2;
+    const size_t row = (size_t)b * a.num_q_heads + (size_t)g * G + h;
+    if (S == 1) {
+      u32x2 w2 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      *reinterpret_cast<u32x2*>(a.o + row * D + d4) = w2;
+      if (a.lse != nullptr && d4 == 0) a.lse[row] = lse;
+    } else {
+      *reinterpret_cast<f32x4*>(a.part_o + (row * S + split) * D + d4) = o;
+      if (d4 == 0) a.part_lse[row * S + split] = lse;
+    }
+  }
+}
+
+}  // namespace miattn

@@ -1,0 +1,354 @@
+// libmiattn host library: argument validation, work planning, workspace and
+// kernel launches behind the C ABI declared in include/miattn.h.
+#include "../../include/miattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+
+#include "combine.h"
+#include "decode.h"
+#include "prefill.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return MIATTN_OK;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_mu;
+int g_arch_ok[kMaxDevices];          // 0 unknown, 1 gfx950, -1 other
+void* g_ws[kMaxDevices];
+size_t g_ws_bytes[kMaxDevices];
+
+bool arch_is_gfx950(int dev) {
+  hipDeviceProp_t p;
+  if (hipGetDeviceProperties(&p, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  return std::strncmp(p.gcnArchName, "gfx950", 6) == 0;
+}
+
+// Current device, checked to be a gfx950; returns the device index or an
+// error code.
+int current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return fail(MIATTN_ERR_UNSUPPORTED, "no HIP device available");
+  }
+  if (dev >= kMaxDevices) return fail(MIATTN_ERR_UNSUPPORTED, "device index %d too large", dev);
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_arch_ok[dev] == 0) g_arch_ok[dev] = arch_is_gfx950(dev) ? 1 : -1;
+  if (g_arch_ok[dev] < 0) return fail(MIATTN_ERR_UNSUPPORTED, "device %d is not a gfx950", dev);
+  return dev;
+}
+
+int check_launch(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MIATTN_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+  return MIATTN_OK;
+}
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+// --- prefill launches ------------------------------------------------------
+template <int D, int KB, bool CAUSAL>
+void launch_fwd(const miattn::FwdArgs& a, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((miattn::miattn_prefill_fwd_kernel<D, KB, CAUSAL>), dim3(grid), dim3(256), 0, st, a);
+}
+
+template <int D, int KB>
+void launch_fwd_c(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t st) {
+  if (causal) launch_fwd<D, KB, true>(a, grid, st);
+  else launch_fwd<D, KB, false>(a, grid, st);
+}
+
+template <int D>
+void launch_decode(const miattn::DecodeArgs& a, int batch, hipStream_t st) {
+  hipLaunchKernelGGL((miattn::miattn_decode_split_kernel<D>), dim3(a.num_splits, a.num_kv_heads, batch),
+                     dim3(256), 0, st, a);
+}
+
+int split_rule(long total_tokens, long work_units, long cu_count, long wg_per_cu, long block_tokens,
+               long max_splits) {
+  if (total_tokens <= 0 || work_units <= 0 || cu_count <= 0 || wg_per_cu <= 0 || block_tokens <= 0 ||
+      max_splits <= 0)
+    return MIATTN_ERR_INVALID_ARG;
+  const long blocks = (total_tokens + block_tokens - 1) / block_tokens;
+  const long capacity = cu_count * wg_per_cu;
+  long top = max_splits;
+  if (capacity < top) top = capacity;
+  if (blocks < top) top = blocks;
+  double best = 0.0;
+  // pass 1: best efficiency over eligible candidates; pass 2: first within 85%
+  for (int pass = 0; pass < 2; ++pass) {
+    for (long s = 1; s <= top; ++s) {
+      if (s > 1 && (blocks + s - 1) / s == (blocks + s - 2) / (s - 1)) continue;
+      const double ratio = (double)(work_units * s) / (double)capacity;
+      const double eff = ratio / std::ceil(ratio);
+      if (pass == 0) {
+        if (eff > best) best = eff;
+      } else if (eff >= 0.85 * best) {
+        return (int)s;
+      }
+    }
+  }
+  return 1;
+}
+
+// MI355X decode capacity: 256 compute units, two split workgroups resident per
+// unit, splits counted in 16-token pages, at most 256 splits.
+constexpr int kCUs = 256;
+constexpr int kDecodeWgPerCu = 2;
+constexpr int kMaxSplits = 256;
+
+}  // namespace
+
+extern "C" {
+
+int miattn_version(void) { return 100; }
+
+const char* miattn_last_error(void) { return g_last_error.c_str(); }
+
+int miattn_device_supported(int device) {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  if (device < 0 || device >= n || device >= kMaxDevices) return 0;
+  return arch_is_gfx950(device) ? 1 : 0;
+}
+
+void miattn_release(void) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) {
+    (void)hipGetLastError();
+    return;
+  }
+  for (int d = 0; d < kMaxDevices; ++d) {
+    if (g_ws[d] != nullptr) {
+      (void)hipSetDevice(d);
+      (void)hipFree(g_ws[d]);
+      g_ws[d] = nullptr;
+      g_ws_bytes[d] = 0;
+    }
+  }
+  (void)hipSetDevice(cur);
+}
+
+int miattn_split_heuristic(int total_tokens, int work_units, int cu_count, int wg_per_cu, int block_tokens,
+                           int max_splits) {
+  const int r = split_rule(total_tokens, work_units, cu_count, wg_per_cu, block_tokens, max_splits);
+  if (r < 0) return fail(r, "split heuristic: all arguments must be positive");
+  return r;
+}
+
+int miattn_decode_pick_splits(int batch, int num_kv_heads, int max_seq_len) {
+  if (batch <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return 1;
+  return split_rule(max_seq_len, (long)batch * num_kv_heads, kCUs, kDecodeWgPerCu, MIATTN_PAGE_SIZE,
+                    kMaxSplits);
+}
+
+size_t miattn_decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 1) return 0;
+  const size_t rows = (size_t)batch * num_q_heads;
+  const size_t bytes = rows * (size_t)num_splits * ((size_t)head_dim + 1) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                    int num_q_heads, int num_kv_heads, int head_dim, float scale, int causal, int dtype,
+                    void* stream) {
+  if (num_seqs < 0 || max_seqlen < 0 || total_tokens < 0)
+    return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: negative size");
+  if (num_seqs == 0 || total_tokens == 0) return ok();
+  if (!q || !k || !v || !o || !cu_seqlens) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: null pointer");
+  if (max_seqlen <= 0) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: max_seqlen must be > 0");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: need Hq > 0, Hkv > 0 and Hq %% Hkv == 0");
+  if (causal != 0 && causal != 1) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: causal must be 0 or 1");
+  if (!scale_ok(scale)) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: scale must be finite and > 0");
+  if (dtype != MIATTN_BF16 && dtype != MIATTN_FP32)
+    return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd: unknown dtype %d", dtype);
+  const int G = num_q_heads / num_kv_heads;
+  if (dtype == MIATTN_BF16) {
+    if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+      return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd: bf16 head_dim must be 64, 128 or 256");
+    if (!(G == 1 || G == 2 || G % 4 == 0))
+      return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd: Hq/Hkv must be 1, 2 or a multiple of 4");
+  } else if (head_dim != 64) {
+    return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd: fp32 head_dim must be 64");
+  }
+  const int dev = current_device();
+  if (dev < 0) return dev;
+  hipStream_t st = (hipStream_t)stream;
+  const float c = scale * miattn::kLog2e;
+
+  if (dtype == MIATTN_FP32) {
+    miattn::FwdF32Args a;
+    a.q = (const float*)q; a.k = (const float*)k; a.v = (const float*)v;
+    a.o = (float*)o; a.lse = lse; a.cu_seqlens = cu_seqlens;
+    a.num_seqs = num_seqs; a.total_tokens = total_tokens;
+    a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
+    a.n_qtiles = (max_seqlen + 31) / 32; a.c = c;
+    const long grid = (long)num_q_heads * num_seqs * a.n_qtiles;
+    if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: problem too large");
+    if (causal)
+      hipLaunchKernelGGL((miattn::miattn_prefill_fwd_f32_kernel<true>), dim3((unsigned)grid), dim3(64), 0, st, a);
+    else
+      hipLaunchKernelGGL((miattn::miattn_prefill_fwd_f32_kernel<false>), dim3((unsigned)grid), dim3(64), 0, st, a);
+    const int r = check_launch("prefill fp32");
+    return r ? r : ok();
+  }
+
+  miattn::FwdArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.o = (uint16_t*)o; a.lse = lse; a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs; a.total_tokens = total_tokens;
+  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
+  a.heads_per_wg = G >= 4 ? 4 : G;
+  const int QR = 32 * (4 / a.heads_per_wg);
+  a.n_qtiles = (max_seqlen + QR - 1) / QR;
+  a.n_head_slots = num_kv_heads * (G / a.heads_per_wg);
+  a.c = c;
+  const long grid = (long)a.n_head_slots * num_seqs * a.n_qtiles;
+  if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: problem too large");
+  const bool cz = causal != 0;
+  switch (head_dim) {
+    case 64: launch_fwd_c<64, 2>(a, (int)grid, cz, st); break;
+    case 128: launch_fwd_c<128, 2>(a, (int)grid, cz, st); break;
+    default: launch_fwd_c<256, 1>(a, (int)grid, cz, st); break;
+  }
+  const int r = check_launch("prefill bf16");
+  return r ? r : ok();
+}
+
+int miattn_attn_combine(const float* partial_o, const float* partial_lse, int rows, int num_splits,
+                        int head_dim, void* o, float* lse, int out_dtype, void* stream) {
+  if (rows < 0) return fail(MIATTN_ERR_INVALID_ARG, "attn_combine: rows < 0");
+  if (num_splits < 1) return fail(MIATTN_ERR_INVALID_ARG, "attn_combine: num_splits must be >= 1");
+  if (head_dim < 4 || head_dim > 1024 || head_dim % 4 != 0)
+    return fail(MIATTN_ERR_UNSUPPORTED, "attn_combine: head_dim must be a multiple of 4 in [4, 1024]");
+  if (out_dtype != MIATTN_BF16 && out_dtype != MIATTN_FP32)
+    return fail(MIATTN_ERR_UNSUPPORTED, "attn_combine: unknown out_dtype %d", out_dtype);
+  if (rows == 0) return ok();
+  if (!partial_o || !partial_lse || !o) return fail(MIATTN_ERR_INVALID_ARG, "attn_combine: null pointer");
+  const int dev = current_device();
+  if (dev < 0) return dev;
+  miattn::CombineArgs a;
+  a.part_o = partial_o; a.part_lse = partial_lse; a.o = o; a.lse = lse;
+  a.rows = rows; a.num_splits = num_splits; a.head_dim = head_dim; a.out_bf16 = out_dtype == MIATTN_BF16;
+  hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3(rows), dim3(256), 0, (hipStream_t)stream, a);
+  const int r = check_launch("combine");
+  return r ? r : ok();
+}
+
+int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, int batch,
+                             int max_pages_per_seq, int page_size, int num_pages, int num_q_heads,
+                             int num_kv_heads, int head_dim, float scale, int num_splits, void* workspace,
+                             size_t workspace_bytes, void* o, float* lse, void* stream) {
+  if (batch < 0) return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: batch < 0");
+  if (num_splits < 0) return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: num_splits < 0");
+  if (page_size != MIATTN_PAGE_SIZE)
+    return fail(MIATTN_ERR_UNSUPPORTED, "attn_decode_paged: page_size must be %d", MIATTN_PAGE_SIZE);
+  if (batch == 0) return ok();
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
+    return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: null pointer");
+  if (max_pages_per_seq <= 0 || num_pages <= 0)
+    return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: max_pages_per_seq and num_pages must be > 0");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: need Hq > 0, Hkv > 0 and Hq %% Hkv == 0");
+  if (num_q_heads / num_kv_heads > miattn::kDecodeMaxGroup)
+    return fail(MIATTN_ERR_UNSUPPORTED, "attn_decode_paged: Hq/Hkv must be <= %d", miattn::kDecodeMaxGroup);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(MIATTN_ERR_UNSUPPORTED, "attn_decode_paged: head_dim must be 64, 128 or 256");
+  if (!scale_ok(scale)) return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: scale must be finite and > 0");
+  if (batch > 65535 || num_kv_heads > 65535)
+    return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: batch and Hkv must be <= 65535");
+  int S = num_splits;
+  if (S == 0) S = miattn_decode_pick_splits(batch, num_kv_heads, max_pages_per_seq * MIATTN_PAGE_SIZE);
+  if (S > max_pages_per_seq) S = max_pages_per_seq;   // more splits than pages would only add empty groups
+  if (S < 1) S = 1;
+  const size_t need = miattn_decode_workspace_bytes(batch, num_q_heads, head_dim, S);
+  if (workspace != nullptr && workspace_bytes < need)
+    return fail(MIATTN_ERR_WORKSPACE, "attn_decode_paged: workspace of %zu bytes, need %zu", workspace_bytes,
+                need);
+  const int dev = current_device();
+  if (dev < 0) return dev;
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (need > 0 && ws == nullptr) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    if (g_ws_bytes[dev] < need) {
+      if (g_ws[dev] != nullptr) {
+        // an enqueued kernel may still read the old buffer
+        if (hipDeviceSynchronize() != hipSuccess || hipFree(g_ws[dev]) != hipSuccess) {
+          (void)hipGetLastError();
+          return fail(MIATTN_ERR_HIP, "attn_decode_paged: releasing the workspace failed");
+        }
+        g_ws[dev] = nullptr;
+        g_ws_bytes[dev] = 0;
+      }
+      if (hipMalloc(&g_ws[dev], need) != hipSuccess) {
+        (void)hipGetLastError();
+        g_ws[dev] = nullptr;
+        return fail(MIATTN_ERR_HIP, "attn_decode_paged: workspace allocation of %zu bytes failed", need);
+      }
+      g_ws_bytes[dev] = need;
+    }
+    ws = g_ws[dev];
+  }
+  miattn::DecodeArgs a;
+  a.q = (const uint16_t*)q; a.k_cache = (const uint16_t*)k_cache; a.v_cache = (const uint16_t*)v_cache;
+  a.block_table = block_table; a.seq_lens = seq_lens;
+  const size_t rows = (size_t)batch * num_q_heads;
+  a.part_o = S > 1 ? (float*)ws : nullptr;
+  a.part_lse = S > 1 ? (float*)ws + rows * (size_t)S * head_dim : nullptr;
+  a.o = (uint16_t*)o; a.lse = lse;
+  a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
+  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = num_q_heads / num_kv_heads;
+  a.num_splits = S; a.c = scale * miattn::kLog2e;
+  switch (head_dim) {
+    case 64: launch_decode<64>(a, batch, st); break;
+    case 128: launch_decode<128>(a, batch, st); break;
+    default: launch_decode<256>(a, batch, st); break;
+  }
+  int r = check_launch("decode split");
+  if (r) return r;
+  if (S > 1) {
+    miattn::CombineArgs c;
+    c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
+    c.rows = (int)rows; c.num_splits = S; c.head_dim = head_dim; c.out_bf16 = 1;
+    hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3((unsigned)rows), dim3(256), 0, st, c);
+    r = check_launch("combine");
+    if (r) return r;
+  }
+  return ok();
+}
+
+}  // extern "C"

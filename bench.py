@@ -1,0 +1,218 @@
+"""Throughput of the attention hot path on one MI355X.
+
+One step runs every stage of the path once on resident synthetic inputs:
+  1. causal GQA prefill, Hq=32, Hkv=8, D=128, S=4096, bf16 (the workload the
+     headline TFLOP/s is quoted on);
+  2. paged split-KV decode + combine, 64 sequences with contexts uniform in
+     [512, 4096], shuffled 16-token pages, Hq=32, Hkv=8, D=128;
+  3. long-context split-KV decode + combine, B=1, Hq=16, Hkv=4, D=256,
+     131072 cached tokens.
+`value` is the prefill TFLOP/s (algorithmic causal FLOPs / prefill time);
+the decodes are reported as KV-read GB/s in the same JSON line. Each kernel
+call is bracketed by HIP events on the stream it runs on.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "attention TFLOP/s (prefill); decode KV-read GB/s; % of MI355X roofline"
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "attention_attn_fwd_03_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_key: str, launches_bytes_alg: float):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; otherwise None."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        with open(p) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = rec.get(kernel_key)
+    if not ent or ent.get("source_hash") != kernel_source_hash():
+        return None
+    return ent.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(prefill_case, heads_sample: int = 8):
+    """The fp64 oracle timed on the host cores on a bounded sample of the
+    prefill workload (the first `heads_sample` query heads)."""
+    import oracle
+    from attention_attn_fwd_03_amd import accounting
+    q, k, v = prefill_case.as_f64()
+    Hkv_s = max(1, heads_sample * prefill_case.num_kv_heads // prefill_case.num_q_heads)
+    qs = np.ascontiguousarray(q[:, :heads_sample])
+    ks = np.ascontiguousarray(k[:, :Hkv_s])
+    vs = np.ascontiguousarray(v[:, :Hkv_s])
+    t0 = time.perf_counter()
+    oracle.attention_dense(qs, ks, vs, prefill_case.cu_seqlens, heads_sample, Hkv_s, prefill_case.scale, True)
+    dt = time.perf_counter() - t0
+    fl = accounting.prefill_flops(prefill_case.seqlens, heads_sample, prefill_case.head_dim, True)
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"causal GQA prefill S={prefill_case.total_tokens}, D={prefill_case.head_dim}, "
+                      f"{heads_sample} of {prefill_case.num_q_heads} query heads ({Hkv_s} kv heads), "
+                      f"fp64 numpy materialized form, {dt:.2f} s; host has "
+                      f"{len(os.sched_getaffinity(0))} usable cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-splits", type=int, default=0, help="0 = library policy")
+    ap.add_argument("--long-splits", type=int, default=0, help="0 = library policy")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
+                                   "not implemented", "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import torch
+    import attention_attn_fwd_03_amd as mi
+    import synth
+    from attention_attn_fwd_03_amd import accounting
+
+    dev = torch.device("cuda:0")
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    pc = synth.config2(S=4096, seed=0)
+    dc = synth.config3(seed=0, tail="zero")
+    lc = synth.config4(ctx=131072, seed=0)
+
+    P = dict(q=bf16(pc.q), k=bf16(pc.k), v=bf16(pc.v), cu=i32(pc.cu_seqlens))
+    P["o"] = torch.empty_like(P["q"])
+    P["lse"] = torch.empty((pc.num_q_heads, pc.total_tokens), dtype=torch.float32, device=dev)
+    Dd = dict(q=bf16(dc.q), kc=bf16(dc.k_cache), vc=bf16(dc.v_cache), bt=i32(dc.block_table), sl=i32(dc.seq_lens))
+    Dd["o"] = torch.empty_like(Dd["q"])
+    Dd["lse"] = torch.empty((dc.batch, dc.num_q_heads), dtype=torch.float32, device=dev)
+    Ld = dict(q=bf16(lc.q), kc=bf16(lc.k_cache), vc=bf16(lc.v_cache), bt=i32(lc.block_table), sl=i32(lc.seq_lens))
+    Ld["o"] = torch.empty_like(Ld["q"])
+    Ld["lse"] = torch.empty((lc.batch, lc.num_q_heads), dtype=torch.float32, device=dev)
+    dsplits = args.decode_splits or mi.decode_pick_splits(dc.batch, dc.num_kv_heads, dc.max_pages * 16)
+    lsplits = args.long_splits or mi.decode_pick_splits(lc.batch, lc.num_kv_heads, lc.max_pages * 16)
+
+    def prefill():
+        mi.attn_fwd(P["q"], P["k"], P["v"], P["cu"], pc.max_seqlen, scale=pc.scale, causal=True,
+                    out=P["o"], lse=P["lse"])
+
+    def decode():
+        mi.attn_decode_paged(Dd["q"], Dd["kc"], Dd["vc"], Dd["bt"], Dd["sl"], scale=dc.scale,
+                             num_splits=dsplits, out=Dd["o"], lse=Dd["lse"])
+
+    def long_decode():
+        mi.attn_decode_paged(Ld["q"], Ld["kc"], Ld["vc"], Ld["bt"], Ld["sl"], scale=lc.scale,
+                             num_splits=lsplits, out=Ld["o"], lse=Ld["lse"])
+
+    stages = [prefill, decode, long_decode]
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        for f in stages:
+            f()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        ev[s][0].record(stream)
+        for i, f in enumerate(stages):
+            f()
+            ev[s][i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = np.array([[ev[s][i].elapsed_time(ev[s][i + 1]) for i in range(len(stages))] for s in range(args.steps)])
+    t_pre, t_dec, t_long = (float(np.mean(per[:, i])) * 1e-3 for i in range(3))
+    step_ms = float(np.mean(per.sum(axis=1)))
+
+    fl_pre = accounting.prefill_flops(pc.seqlens, pc.num_q_heads, pc.head_dim, True)
+    tflops = fl_pre / t_pre / 1e12
+    by_dec = accounting.decode_bytes(dc.seq_lens, dc.num_q_heads, dc.num_kv_heads, dc.head_dim)
+    by_long = accounting.decode_bytes(lc.seq_lens, lc.num_q_heads, lc.num_kv_heads, lc.head_dim)
+    gbs_dec = by_dec / t_dec / 1e9
+    gbs_long = by_long / t_long / 1e9
+
+    traffic = traffic_from_profile("prefill_causal_gqa_s4096", accounting.prefill_bytes(4096, 32, 8, 128))
+    line = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1), rounded to bf16)",
+        "config": {
+            "workload": "causal GQA prefill Hq=32 Hkv=8 D=128 S=4096 + paged decode B=64 ctx U[512,4096] "
+                        "shuffled 16-token pages + long decode B=1 Hq=16 Hkv=4 D=256 ctx=131072",
+            "prefill": {"S": 4096, "Hq": 32, "Hkv": 8, "D": 128, "causal": True, "ms": round(t_pre * 1e3, 4),
+                        "algorithmic_gflop": round(fl_pre / 1e9, 3)},
+            "decode_paged": {"B": dc.batch, "tokens": int(dc.seq_lens.sum()), "splits": dsplits,
+                             "ms": round(t_dec * 1e3, 4), "GB/s": round(gbs_dec, 1),
+                             "frac_hbm": round(gbs_dec / PEAK_HBM_GBS, 4), "algorithmic_MB": round(by_dec / 1e6, 2)},
+            "decode_long": {"ctx": 131072, "splits": lsplits, "ms": round(t_long * 1e3, 4),
+                            "GB/s": round(gbs_long, 1), "frac_hbm": round(gbs_long / PEAK_HBM_GBS, 4),
+                            "algorithmic_MB": round(by_long / 1e6, 2)},
+            "wall_s": round(wall, 4),
+        },
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "miattn_prefill_fwd_kernel<128,2,true>",
+                     "per_launch_work": f"{fl_pre:.6g} FLOP"},
+        "roofline_decode": {"bound": "hbm", "achieved": round(gbs_long, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(gbs_long / PEAK_HBM_GBS, 4),
+                            "traffic": traffic_from_profile("decode_long_ctx131072", by_long),
+                            "kernel": "miattn_decode_split_kernel<256> + miattn_combine_kernel",
+                            "per_launch_work": f"{by_long:.6g} B"},
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(pc)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

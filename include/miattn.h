@@ -1,0 +1,176 @@
+/*
+ * libmiattn -- tiled scaled-dot-product attention with an online softmax for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one defined in "Why your local LLM feels dumber than it
+ * is" (section "What attention is trying to calculate"): for a query row i of
+ * head h and the keys J(i) it may see,
+ *     s_ij = scale * dot(q_i, k_j),   O_i = sum_j exp(s_ij) v_j / sum_j exp(s_ij),
+ *     LSE_i = ln sum_j exp(s_ij)      (natural log, in units of the scaled score).
+ * It is evaluated tile by tile without materialising the scores, with the
+ * running max / running sum rescaling of "Streaming process" (steps 3-8 and its
+ * code snippet); the result equals the definition up to rounding order.
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     keeps none of them after the call returns. Layouts are row-major with the
+ *     last dimension contiguous.
+ *   - Query head h reads key/value head g = h / (Hq / Hkv) (contiguous groups).
+ *   - `stream` is a hipStream_t (NULL = the default stream). A return value of
+ *     MIATTN_OK means the work was enqueued; results are valid once the stream
+ *     has been synchronised. The library performs no device synchronisation
+ *     and no device-to-host reads.
+ *   - All arguments are validated on the host before any HIP call; an invalid
+ *     call returns an error code, enqueues nothing and leaves no sticky HIP
+ *     error. miattn_last_error() describes the most recent failure of the
+ *     calling thread.
+ *   - For a fixed problem (shapes, page size and split count) the outputs are
+ *     bitwise identical from run to run: no floating-point atomics are used and
+ *     every reduction has a fixed order.
+ *   - Inputs are not checked for NaN/Inf; non-finite inputs propagate.
+ */
+#ifndef MIATTN_H
+#define MIATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* return codes */
+#define MIATTN_OK                 0
+#define MIATTN_ERR_INVALID_ARG   (-1)  /* bad pointer, size or flag              */
+#define MIATTN_ERR_UNSUPPORTED   (-2)  /* dtype / head_dim / device not handled  */
+#define MIATTN_ERR_HIP           (-3)  /* a HIP call or kernel launch failed     */
+#define MIATTN_ERR_WORKSPACE     (-4)  /* caller workspace smaller than needed   */
+
+/* element types */
+#define MIATTN_BF16 0
+#define MIATTN_FP32 1
+
+#define MIATTN_PAGE_SIZE 16            /* tokens per KV-cache page               */
+
+/*
+ * miattn_attn_fwd -- prefill / dense forward over packed variable-length
+ * sequences (FlashAttention forward: "Streaming process" steps 3-8 and code
+ * snippet; the causal GQA cells of "GPU Datapath: Where Every Byte Moves",
+ * section C; varlen packing through cu_seqlens as in that page's section
+ * "Measuring the Real Kernels, One at a Time").
+ *
+ *   q    [total_tokens, Hq,  D]  dtype
+ *   k, v [total_tokens, Hkv, D]  dtype
+ *   o    [total_tokens, Hq,  D]  dtype        (written)
+ *   lse  [Hq, total_tokens]      float32      (written; may be NULL)
+ *   cu_seqlens [num_seqs + 1]    int32, device; sequence b occupies token rows
+ *        [cu_seqlens[b], cu_seqlens[b+1]). Must be non-decreasing, start at 0
+ *        and end at total_tokens, and no sequence may exceed max_seqlen. Rows
+ *        outside these promises are clamped so that no access leaves the
+ *        buffers, but their results are unspecified.
+ *   num_seqs, max_seqlen, total_tokens: host integers that size the grid.
+ *   scale: finite and > 0 (scores are scale * q.k).
+ *   causal: 0 = every key of the sequence; 1 = key j <= query i (positions
+ *        counted from each sequence's start; queries and keys coincide).
+ *   dtype: MIATTN_BF16 with head_dim 64, 128 or 256, or MIATTN_FP32 with
+ *        head_dim 64. bf16 inputs are multiplied on bf16 MFMA with fp32
+ *        accumulation; softmax state is fp32; the probabilities enter the P.V
+ *        product rounded to bf16 and O is rounded to bf16 once at the end.
+ *        fp32 inputs stay fp32 throughout (fp32 MFMA).
+ *   LSE_i = max_j s_ij + ln sum_j exp(s_ij - max_j s_ij).
+ * num_seqs == 0 or total_tokens == 0 is a no-op returning MIATTN_OK.
+ */
+int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens,
+                    int num_q_heads, int num_kv_heads, int head_dim, float scale, int causal,
+                    int dtype, void* stream);
+
+/*
+ * miattn_attn_decode_paged -- one query token per sequence against a paged
+ * KV cache ("GPU Datapath", section D: block table of 16-token pages, pages in
+ * any order), evaluated split-KV: the context of each sequence is cut into
+ * num_splits contiguous, page-aligned groups of ceil(pages / num_splits)
+ * pages, each group yields a normalised partial output and its log-sum-exp,
+ * and the groups are merged by log-sum-exp weights ("Why your local LLM feels
+ * dumber than it is", sections "Why the calculation is split into groups" and
+ * "Backend names expand into four decode algorithms", FlashAttention 2 entry).
+ *
+ *   q        [batch, Hq, D]                         bf16
+ *   k_cache, v_cache [num_pages, 16, Hkv, D]        bf16
+ *   block_table [batch, max_pages_per_seq]          int32, device: logical page
+ *            p of sequence b is physical page block_table[b, p]
+ *   seq_lens [batch]                                int32, device: tokens
+ *            cached for each sequence (the query sees all of them)
+ *   o        [batch, Hq, D] bf16 (written); lse [batch, Hq] float32 (written;
+ *            may be NULL). A sequence of length 0 gives o = 0, lse = -inf.
+ *   page_size must be MIATTN_PAGE_SIZE; head_dim 64, 128 or 256; Hq/Hkv <= 16.
+ *   num_splits: >= 1 to fix the split count, 0 to let the library choose
+ *            (miattn_decode_pick_splits). Bitwise reproducibility holds for a
+ *            fixed split count.
+ *   workspace / workspace_bytes: device scratch for the split partials
+ *            (miattn_decode_workspace_bytes bytes). workspace == NULL uses a
+ *            buffer the library allocates and caches per device (grown on
+ *            demand; freed by miattn_release). Not used when the split count
+ *            is 1.
+ * Robustness: seq_lens are clamped to [0, max_pages_per_seq * 16]; a block
+ * table entry outside [0, num_pages) makes that page contribute nothing. Such
+ * inputs never fault, but their results are unspecified.
+ */
+int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens,
+                             int batch, int max_pages_per_seq, int page_size, int num_pages,
+                             int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                             int num_splits, void* workspace, size_t workspace_bytes,
+                             void* o, float* lse, void* stream);
+
+/*
+ * miattn_attn_combine -- merge split partials by log-sum-exp weights (the
+ * FlashAttention 2 merge of "Why your local LLM feels dumber than it is",
+ * section "Backend names expand into four decode algorithms"):
+ *     M = max_s LSE_s over non-empty splits, w_s = exp(LSE_s - M),
+ *     O = sum_s w_s O_s / sum_s w_s,   LSE = M + ln sum_s w_s,
+ * splits taken in the fixed order s = 0 .. num_splits-1. A split with
+ * LSE_s = -inf is empty and skipped; a row whose splits are all empty gives
+ * O = 0, LSE = -inf.
+ *   partial_o   [rows, num_splits, D] float32 (normalised partial outputs)
+ *   partial_lse [rows, num_splits]    float32
+ *   o [rows, D] of out_dtype (MIATTN_BF16 or MIATTN_FP32); lse [rows] float32
+ *   (may be NULL). D: 1 .. 1024 and a multiple of 4. rows == 0 is a no-op.
+ */
+int miattn_attn_combine(const float* partial_o, const float* partial_lse, int rows,
+                        int num_splits, int head_dim, void* o, float* lse, int out_dtype,
+                        void* stream);
+
+/* Bytes of workspace miattn_attn_decode_paged needs for the partials
+ * (0 when num_splits <= 1). */
+size_t miattn_decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int num_splits);
+
+/* Split count chosen for num_splits == 0: the FlashAttention-2-shaped rule
+ * of miattn_split_heuristic with this library's MI355X capacity (256 compute
+ * units, decode workgroups resident per unit) and 16-token pages as blocks. */
+int miattn_decode_pick_splits(int batch, int num_kv_heads, int max_seq_len);
+
+/* The split-count rule described in "Why your local LLM feels dumber than it
+ * is", section "Why FlashAttention 2 selects 54, 62, or 87 groups": capacity =
+ * cu_count * wg_per_cu; a candidate s scores work_units * s / capacity and
+ * efficiency ratio / ceil(ratio); candidates that do not change the blocks per
+ * split are skipped; the smallest candidate within 85% of the best efficiency
+ * wins; candidates run from 1 to min(max_splits, capacity, blocks).
+ * Returns the split count, or MIATTN_ERR_INVALID_ARG for non-positive input. */
+int miattn_split_heuristic(int total_tokens, int work_units, int cu_count, int wg_per_cu,
+                           int block_tokens, int max_splits);
+
+/* Thread-local description of the last failure ("" if none). */
+const char* miattn_last_error(void);
+/* Library version: major * 10000 + minor * 100 + patch. */
+int miattn_version(void);
+/* 1 if HIP device `device` is a gfx950 the kernels were built for, else 0. */
+int miattn_device_supported(int device);
+/* Free the library-owned workspace cache on every device (safe to call at any
+ * time when no call is in flight). */
+void miattn_release(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MIATTN_H */

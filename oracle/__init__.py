@@ -34,6 +34,7 @@ project's design notes.
 from .reference import (  # noqa: F401
     attention_dense,
     attention_brute,
+    attention_rows,
     decode_dense,
     decode_brute,
     gather_sequence_kv,

@@ -115,6 +115,33 @@ def attention_brute(q, k, v, cu_seqlens, num_q_heads: int, num_kv_heads: int,
     return O, LSE
 
 
+def attention_rows(q, k, v, cu_seqlens, num_q_heads: int, num_kv_heads: int,
+                   scale: float, causal: bool, token_rows):
+    """The same definition evaluated only for the listed packed token rows
+    (for spot checks of problems too large to materialize). Returns
+    O [n, Hq, D] and LSE [Hq, n] for the rows in the order given."""
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    cu = np.asarray(cu_seqlens, dtype=np.int64)
+    group = num_q_heads // num_kv_heads
+    rows = [int(t) for t in token_rows]
+    O = np.zeros((len(rows), num_q_heads, v.shape[2]))
+    LSE = np.full((num_q_heads, len(rows)), NEG_INF)
+    for n, t in enumerate(rows):
+        b = int(np.searchsorted(cu, t, side="right")) - 1
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        hi = t + 1 if causal else s1
+        for h in range(num_q_heads):
+            g = h // group
+            Kb = np.asarray(k[s0:hi, g, :], dtype=np.float64)
+            S = (scale * (Kb @ np.asarray(q[t, h, :], dtype=np.float64)))[None, :]
+            o, l = _softmax_rows(S, np.asarray(v[s0:hi, g, :], dtype=np.float64))
+            O[n, h] = o[0]
+            LSE[h, n] = l[0]
+    return O, LSE
+
+
 # --------------------------------------------------------------------------
 # paged decode ("GPU Datapath", section D: one query token per sequence, the
 # KV cache read through a block table of 16-token pages)

@@ -1,0 +1,61 @@
+"""Helpers for the GPU parity tests (test side only)."""
+import numpy as np
+import torch
+
+DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
+
+BF16_MAX_ABS = 1e-2
+BF16_MEAN_ABS = 1e-3
+FP32_MAX_ABS = 1e-5
+LSE_MAX_ABS = 1e-3
+
+
+def bf16_dev(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(DEV)
+
+
+def f32_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(DEV)
+
+
+def i32_dev(x):
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).to(DEV)
+
+
+def host(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def errors(got, want):
+    e = np.abs(got - want)
+    return float(e.max()) if e.size else 0.0, float(e.mean()) if e.size else 0.0
+
+
+def assert_bf16_close(got, want, what=""):
+    mx, mean = errors(got, want)
+    print(f"  {what}: max-abs {mx:.3e} mean-abs {mean:.3e}", flush=True)
+    assert mx <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (what, mx, mean)
+
+
+def assert_bf16_rounding_of(got, want, slop=2e-5, what=""):
+    """got is a bf16 result whose exact value is `want`: allow half a bf16 ulp
+    of |want| (round to nearest) plus the fp32 arithmetic slop."""
+    a = np.maximum(np.abs(want), np.abs(got))
+    ulp = np.where(a > 0, np.exp2(np.floor(np.log2(np.where(a > 0, a, 1.0))) - 7), 0.0)
+    bad = np.abs(got - want) > 0.5 * ulp + slop
+    print(f"  {what}: {int(bad.sum())} elements beyond half a bf16 ulp", flush=True)
+    assert not bad.any(), what
+
+
+def assert_lse_close(got, want, what=""):
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin), what
+    assert np.array_equal(got[~fin], want[~fin]), what
+    mx, _ = errors(got[fin], want[fin])
+    print(f"  {what} lse: max-abs {mx:.3e}", flush=True)
+    assert mx <= LSE_MAX_ABS, (what, mx)
+
+
+def bitwise_equal(a, b):
+    return torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
+                       b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))

@@ -1,0 +1,164 @@
+"""Paged split-KV decode parity against the fp64 oracle, split-count
+agreement, bitwise repeatability and layout invariances."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import attention_attn_fwd_03_amd as mi
+import oracle
+import synth
+from gpu_util import (assert_bf16_close, assert_lse_close, bf16_dev, bitwise_equal, errors, host, i32_dev)
+
+pytestmark = pytest.mark.gpu
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def to_dev(case):
+    return (bf16_dev(case.q), bf16_dev(case.k_cache), bf16_dev(case.v_cache), i32_dev(case.block_table),
+            i32_dev(case.seq_lens))
+
+
+def run(case, S, dev_args=None, **kw):
+    args = dev_args or to_dev(case)
+    o, l = mi.attn_decode_paged(*args, scale=case.scale, num_splits=S, **kw)
+    torch.cuda.synchronize()
+    return o, l
+
+
+def reference(case):
+    q, kc, vc = case.as_f64()
+    return oracle.decode_dense(q, kc, vc, case.block_table, case.seq_lens, case.scale)
+
+
+@pytest.mark.parametrize("S", [1, 2, 5, 0])
+def test_small_batch_nan_tails(S):
+    case = synth.make_decode(3, 1, [1, 15, 16, 17, 100, 300, 33, 64], 32, 8, 128, 1 / math.sqrt(128),
+                             shuffle=True, tail="nan", name="small_nan_tails")
+    print(f"[decode] {case.name} S={S}", flush=True)
+    o, l = run(case, S)
+    O, L = reference(case)
+    assert_bf16_close(host(o), O, f"S={S}")
+    assert_lse_close(host(l), L, f"S={S}")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_paged_decode_full_size(seed):
+    case = synth.config3(seed=seed)
+    print(f"[decode] {case.name} seed={seed} policy split={mi.decode_pick_splits(64, 8, case.max_pages * 16)}",
+          flush=True)
+    dev = to_dev(case)
+    O, L = reference(case)
+    for S in (0, 1, 4):
+        o, l = run(case, S, dev)
+        assert_bf16_close(host(o), O, f"S={S}")
+        assert_lse_close(host(l), L, f"S={S}")
+
+
+@pytest.mark.parametrize("ctx", [16384, 131072])
+def test_long_context_split_agreement(ctx):
+    case = synth.config4(ctx=ctx, seed=0)
+    print(f"[decode] {case.name}", flush=True)
+    dev = to_dev(case)
+    O, L = reference(case)
+    outs = {}
+    for S in (1, 16, 64, 256):
+        o, l = run(case, S, dev)
+        assert_bf16_close(host(o), O, f"ctx={ctx} S={S}")
+        assert_lse_close(host(l), L, f"ctx={ctx} S={S}")
+        o2, l2 = run(case, S, dev)
+        assert bitwise_equal(o, o2) and bitwise_equal(l, l2), f"not bitwise repeatable at S={S}"
+        outs[S] = host(o)
+    for a in outs:
+        for b in outs:
+            if a < b:
+                mx, mean = errors(outs[a], outs[b])
+                assert mx <= 1e-2 and mean <= 1e-3, (a, b, mx, mean)
+
+
+@pytest.mark.parametrize("ctx", [32768, 65536])
+def test_long_context_middle_sizes(ctx):
+    case = synth.config4(ctx=ctx, seed=1)
+    dev = to_dev(case)
+    O, L = reference(case)
+    for S in (0, 64):
+        o, l = run(case, S, dev)
+        assert_bf16_close(host(o), O, f"ctx={ctx} S={S}")
+        assert_lse_close(host(l), L, f"ctx={ctx} S={S}")
+
+
+def test_worked_example():
+    g = json.load(open(os.path.join(GOLD, "worked_example.json")))
+    case = synth.worked_example_decode(head_dim=64)
+    dev = to_dev(case)
+    allowed = {row["bf16_output"] for row in g["platforms"]}
+    for S in (1, 54, 62, 87):
+        o, l = run(case, S, dev)
+        val = float(o[0, 0, 0].float().cpu())
+        print(f"  worked example S={S}: {val!r}", flush=True)
+        assert val in allowed
+        assert abs(val - g["exact_output"]) <= 1e-2
+        assert torch.count_nonzero(o[0, 0, 1:].float()) == 0
+
+
+def test_shuffled_equals_identity_table():
+    ident = synth.make_decode(3, 4, [700, 33, 256], 32, 8, 128, 0.088, shuffle=False, tail="zero")
+    shuf = synth.make_decode(3, 4, [700, 33, 256], 32, 8, 128, 0.088, shuffle=True, tail="zero")
+    for S in (1, 3):
+        oi, li = run(ident, S)
+        os_, ls = run(shuf, S)
+        assert bitwise_equal(oi, os_) and bitwise_equal(li, ls)
+
+
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 128), (8, 1, 64), (16, 2, 256), (6, 3, 128)])
+def test_shapes(Hq, Hkv, D):
+    case = synth.make_decode(30, 0, [50, 1, 129, 400], Hq, Hkv, D, 1 / math.sqrt(D), shuffle=True)
+    O, L = reference(case)
+    for S in (1, 3):
+        o, l = run(case, S)
+        assert_bf16_close(host(o), O, f"{Hq}x{Hkv} D={D} S={S}")
+        assert_lse_close(host(l), L, f"{Hq}x{Hkv} D={D} S={S}")
+
+
+def test_empty_sequence_and_more_splits_than_pages():
+    case = synth.make_decode(31, 0, [40, 3], 8, 2, 128, 0.1, shuffle=True)
+    dev = list(to_dev(case))
+    dev[4] = i32_dev(np.array([0, 3], np.int32))
+    o, l = run(case, 7, tuple(dev))
+    O, L = oracle.decode_dense(*case.as_f64(), case.block_table, np.array([0, 3]), case.scale)
+    assert torch.count_nonzero(o[0].float()) == 0
+    assert torch.all(torch.isneginf(l[0]))
+    assert_bf16_close(host(o), O, "empty seq")
+    assert_lse_close(host(l), L, "empty seq")
+
+
+def test_decode_matches_last_row_of_prefill():
+    L_ = 333
+    pc = synth.make_prefill(32, 0, [L_], 32, 8, 128, 1 / math.sqrt(128), True, "bf16")
+    op, lp = mi.attn_fwd(bf16_dev(pc.q), bf16_dev(pc.k), bf16_dev(pc.v), i32_dev(pc.cu_seqlens), L_,
+                         scale=pc.scale, causal=True)
+    n_pages = (L_ + 15) // 16
+    kc = np.zeros((n_pages * 16, 8, 128), np.uint16); vc = np.zeros_like(kc)
+    kc[:L_] = pc.k; vc[:L_] = pc.v
+    kc = kc.reshape(n_pages, 16, 8, 128); vc = vc.reshape(n_pages, 16, 8, 128)
+    od, ld = mi.attn_decode_paged(bf16_dev(pc.q[L_ - 1:L_]), bf16_dev(kc), bf16_dev(vc),
+                                  i32_dev(np.arange(n_pages)[None]), i32_dev(np.array([L_])), scale=pc.scale,
+                                  num_splits=3)
+    torch.cuda.synchronize()
+    assert_bf16_close(host(od[0]), host(op[L_ - 1]), "decode vs prefill last row")
+    assert np.max(np.abs(host(ld[0]) - host(lp[:, L_ - 1]))) <= 1e-3
+
+
+def test_caller_workspace():
+    case = synth.make_decode(33, 0, [500, 200], 32, 8, 128, 0.09, shuffle=True)
+    n = mi.decode_workspace_bytes(2, 32, 128, 4)
+    ws = torch.empty(n // 4, dtype=torch.float32, device="cuda")
+    o1, l1 = run(case, 4, workspace=ws)
+    o2, l2 = run(case, 4)
+    assert bitwise_equal(o1, o2) and bitwise_equal(l1, l2)
+    small = torch.empty(8, dtype=torch.float32, device="cuda")
+    with pytest.raises(mi.MiattnError):
+        run(case, 4, workspace=small)

@@ -1,0 +1,147 @@
+"""Prefill parity: the HIP kernels against the fp64 oracle on the same seeded
+inputs (bf16: max-abs 1e-2, mean-abs 1e-3; fp32: 1e-5; LSE: 1e-3)."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import attention_attn_fwd_03_amd as mi
+import oracle
+import synth
+from gpu_util import (FP32_MAX_ABS, assert_bf16_close, assert_lse_close, bf16_dev, bitwise_equal, errors,
+                      f32_dev, host, i32_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def run(case, lse=True):
+    dev = f32_dev if case.dtype == "fp32" else bf16_dev
+    o, l = mi.attn_fwd(dev(case.q), dev(case.k), dev(case.v), i32_dev(case.cu_seqlens), case.max_seqlen,
+                       scale=case.scale, causal=case.causal, return_lse=lse)
+    torch.cuda.synchronize()
+    return o, l
+
+
+def full_check(case):
+    print(f"[prefill] {case.name} lens={case.seqlens.tolist()[:8]} Hq={case.num_q_heads} "
+          f"Hkv={case.num_kv_heads} D={case.head_dim} causal={case.causal}", flush=True)
+    o, l = run(case)
+    q, k, v = case.as_f64()
+    O, L = oracle.attention_dense(q, k, v, case.cu_seqlens, case.num_q_heads, case.num_kv_heads, case.scale,
+                                  case.causal)
+    if case.dtype == "fp32":
+        mx, _ = errors(host(o), O)
+        print(f"  fp32 max-abs {mx:.3e}", flush=True)
+        assert mx <= FP32_MAX_ABS
+    else:
+        assert_bf16_close(host(o), O, case.name)
+    assert_lse_close(host(l), L, case.name)
+    return o, l
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_dense_fp32_single_head(seed):
+    full_check(synth.config1(seed))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_causal_gqa_d128_ragged(seed):
+    # spans several 32-row query tiles and 64-key tiles, ragged tail
+    full_check(synth.make_prefill(2, seed, [1000], 32, 8, 128, 1 / math.sqrt(128), True, "bf16", "gqa_s1000"))
+
+
+def test_causal_gqa_d128_s1024_full():
+    full_check(synth.config2(S=1024, seed=0))
+
+
+@pytest.mark.parametrize("S", [2048, 4096])
+def test_causal_gqa_d128_full_size_sampled(S):
+    case = synth.config2(S=S, seed=0)
+    print(f"[prefill] {case.name} sampled rows", flush=True)
+    o, l = run(case)
+    rng = np.random.default_rng(S)
+    rows = np.unique(np.concatenate([[0, 1, 31, 32, 63, 64, S - 1], rng.integers(0, S, 40)]))
+    q, k, v = case.as_f64()
+    O, L = oracle.attention_rows(q, k, v, case.cu_seqlens, 32, 8, case.scale, True, rows)
+    assert_bf16_close(host(o)[rows], O, case.name)
+    assert_lse_close(host(l)[:, rows], L, case.name)
+
+
+def test_varlen_d256_small_full():
+    full_check(synth.make_prefill(5, 0, [1, 17, 100, 257, 64, 33, 300], 16, 4, 256, 2.0 ** -4, True, "bf16",
+                                  "varlen_small_d256"))
+
+
+def test_varlen_d256_full_size_sampled():
+    case = synth.config5(seed=0)
+    print(f"[prefill] {case.name} lens={case.seqlens.tolist()} sampled rows", flush=True)
+    o, l = run(case)
+    cu = case.cu_seqlens
+    rng = np.random.default_rng(5)
+    rows = [int(cu[b]) for b in range(len(cu) - 1)] + [int(cu[b + 1]) - 1 for b in range(len(cu) - 1)]
+    rows += rng.integers(0, case.total_tokens, 24).tolist()
+    rows = np.unique(rows)
+    q, k, v = case.as_f64()
+    O, L = oracle.attention_rows(q, k, v, cu, 16, 4, case.scale, True, rows)
+    assert_bf16_close(host(o)[rows], O, case.name)
+    assert_lse_close(host(l)[:, rows], L, case.name)
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,D,causal", [
+    ([200], 8, 8, 64, False),       # MHA, 4 query blocks per workgroup
+    ([130, 70], 4, 2, 128, True),   # G = 2
+    ([96], 16, 2, 64, True),        # G = 8: two workgroups per kv head
+    ([77, 1, 150], 4, 1, 256, False),
+    ([300], 4, 4, 128, True),
+])
+def test_shapes(lens, Hq, Hkv, D, causal):
+    full_check(synth.make_prefill(20, 0, lens, Hq, Hkv, D, 1 / math.sqrt(D), causal, "bf16",
+                                  f"shape_{Hq}x{Hkv}_d{D}"))
+
+
+def test_zero_length_sequences_and_single_tokens():
+    full_check(synth.make_prefill(21, 0, [0, 1, 0, 5, 1], 8, 2, 128, 0.1, True, "bf16", "degenerate"))
+
+
+def test_bitwise_repeatable():
+    case = synth.config2(S=1024, seed=1)
+    o1, l1 = run(case)
+    for _ in range(5):
+        o2, l2 = run(case)
+        assert bitwise_equal(o1, o2) and bitwise_equal(l1, l2)
+
+
+def test_packed_equals_separate():
+    case = synth.make_prefill(22, 0, [130, 1, 257, 64], 16, 4, 128, 0.09, True, "bf16", "packed")
+    o, l = run(case)
+    cu = case.cu_seqlens
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        sub = synth.PrefillCase("sep", case.q[s0:s1], case.k[s0:s1], case.v[s0:s1],
+                                np.array([0, s1 - s0], np.int32), 16, 4, 128, case.scale, True, "bf16")
+        ob, lb = run(sub)
+        assert bitwise_equal(o[s0:s1], ob)
+        assert bitwise_equal(l[:, s0:s1].contiguous(), lb)
+
+
+def test_lse_optional():
+    case = synth.config2(S=256, seed=0)
+    o, _ = run(case, lse=False)
+    o2, _ = run(case)
+    assert bitwise_equal(o, o2)
+
+
+def test_score_shift_moves_lse_only():
+    # an extra channel with q = c, k = 1 adds scale*c to every score (D 64 -> 128 with zero padding)
+    base = synth.make_prefill(23, 0, [190], 4, 2, 64, 0.125, True, "bf16")
+    T = base.total_tokens
+    q = np.zeros((T, 4, 128), np.uint16); k = np.zeros((T, 2, 128), np.uint16); v = np.zeros((T, 2, 128), np.uint16)
+    q[:, :, :64] = base.q; k[:, :, :64] = base.k; v[:, :, :64] = base.v
+    c0 = synth.PrefillCase("pad", q.copy(), k.copy(), v, base.cu_seqlens, 4, 2, 128, 0.125, True, "bf16")
+    q[:, :, 64] = synth.bf16_bits(np.float32(4.0)); k[:, :, 64] = synth.bf16_bits(np.float32(1.0))
+    c1 = synth.PrefillCase("shift", q, k, v, base.cu_seqlens, 4, 2, 128, 0.125, True, "bf16")
+    o0, l0 = run(c0)
+    o1, l1 = run(c1)
+    assert_bf16_close(host(o1), host(o0), "shifted vs unshifted")
+    assert np.max(np.abs(host(l1) - (host(l0) + 0.5))) <= 1e-3

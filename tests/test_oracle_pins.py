@@ -261,3 +261,16 @@ def test_nan_page_tails_never_reach_results():
     assert np.all(np.isfinite(O)) and np.all(np.isfinite(L))
     po, pl = oracle.decode_split_partials(q, kc, vc, c.block_table, c.seq_lens, c.scale, 3)
     assert np.all(np.isfinite(po))
+
+
+def test_row_sampler_matches_dense():
+    c = synth.make_prefill(111, 0, [40, 9, 23], 4, 2, 8, 0.3, True, "bf16")
+    q, k, v = c.as_f64()
+    O, L = oracle.attention_dense(q, k, v, c.cu_seqlens, 4, 2, c.scale, True)
+    rows = [0, 39, 40, 48, 49, 71, 5]
+    Or, Lr = oracle.attention_rows(q, k, v, c.cu_seqlens, 4, 2, c.scale, True, rows)
+    assert np.max(np.abs(Or - O[rows])) <= 1e-14
+    assert np.max(np.abs(Lr - L[:, rows])) <= 1e-14
+    On, Ln = oracle.attention_rows(q, k, v, c.cu_seqlens, 4, 2, c.scale, False, rows)
+    Od, Ld = oracle.attention_dense(q, k, v, c.cu_seqlens, 4, 2, c.scale, False)
+    assert np.max(np.abs(On - Od[rows])) <= 1e-14
