@@ -3,10 +3,10 @@
 // FlashAttention 2 entry: fp32 normalised partial outputs weighted by
 // exp(LSE_s - max LSE)).
 //
-// One workgroup of 256 threads per output row. Each thread owns four
-// consecutive output columns and a residue class of splits; partial sums are
-// folded through LDS in a fixed order, so the result does not depend on
-// scheduling. Empty splits (LSE = -inf) are skipped; an all-empty row gives
+// Each workgroup owns one output row and up to 128 of its columns; each
+// thread owns four consecutive columns and a residue class of splits. Partial
+// sums are folded through LDS in a fixed order, so the result does not depend
+// on scheduling. Empty splits (LSE = -inf) are skipped; an all-empty row gives
 // O = 0 and LSE = -inf.
 #pragma once
 #include "common.h"
@@ -38,6 +38,11 @@ __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) 
   return r;
 }
 
+constexpr int kCombineCols = 32;   // float4 columns per workgroup (128 output columns)
+constexpr int kCombineUnroll = 8;  // independent partial loads in flight per thread
+
+// Grid: (rows, ceil(D / 128)). Threads: kCombineCols column lanes x NG split
+// groups; group g sums splits g, g + NG, ... in increasing order.
 __global__ __launch_bounds__(256) void miattn_combine_kernel(CombineArgs a) {
   __shared__ float red[256];
   __shared__ f32x4 part[256];
@@ -45,7 +50,9 @@ __global__ __launch_bounds__(256) void miattn_combine_kernel(CombineArgs a) {
   const int S = a.num_splits;
   const int D = a.head_dim;
   const int DQ = D / 4;
-  const int NG = 256 / DQ;
+  const int col0 = blockIdx.y * kCombineCols;
+  const int ncol = DQ - col0 < kCombineCols ? DQ - col0 : kCombineCols;
+  const int NG = 256 / ncol;
   const int t = threadIdx.x;
   const float* pl = a.part_lse + (size_t)row * S;
   const float* po = a.part_o + (size_t)row * S * D;
@@ -62,22 +69,33 @@ __global__ __launch_bounds__(256) void miattn_combine_kernel(CombineArgs a) {
     }
   const float W = block_reduce(ws, red, false);
 
-  const int c = t % DQ;
-  const int gi = t / DQ;
+  const int c = col0 + t % ncol;
+  const int gi = t / ncol;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (!empty && gi < NG) {
-    for (int s = gi; s < S; s += NG) {
-      const float x = pl[s];
-      if (x == kNegInf) continue;
-      const float w = exp2_hw((x - M) * kLog2e);
-      acc += w * *reinterpret_cast<const f32x4*>(po + (size_t)s * D + 4 * c);
+    for (int s0 = gi; s0 < S; s0 += NG * kCombineUnroll) {
+      f32x4 v[kCombineUnroll];
+      float x[kCombineUnroll];
+#pragma unroll
+      for (int u = 0; u < kCombineUnroll; ++u) {
+        const int s = s0 + u * NG;
+        const int sc = s < S ? s : S - 1;
+        x[u] = s < S ? pl[sc] : kNegInf;
+        v[u] = *reinterpret_cast<const f32x4*>(po + (size_t)sc * D + 4 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < kCombineUnroll; ++u) {
+        const float w = exp2_hw((x[u] - M) * kLog2e);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        acc += (x[u] == kNegInf) ? z : w * v[u];
+      }
     }
   }
   part[t] = acc;
   __syncthreads();
   if (gi == 0) {
-    f32x4 sum = part[c];
-    for (int k = 1; k < NG; ++k) sum += part[k * DQ + c];
+    f32x4 sum = part[t];
+    for (int k = 1; k < NG; ++k) sum += part[k * ncol + t];
     const float inv = empty ? 0.f : 1.f / W;
     sum *= inv;
     if (a.out_bf16) {

@@ -262,7 +262,8 @@ int miattn_attn_combine(const float* partial_o, const float* partial_lse, int ro
   miattn::CombineArgs a;
   a.part_o = partial_o; a.part_lse = partial_lse; a.o = o; a.lse = lse;
   a.rows = rows; a.num_splits = num_splits; a.head_dim = head_dim; a.out_bf16 = out_dtype == MIATTN_BF16;
-  hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3(rows), dim3(256), 0, (hipStream_t)stream, a);
+  const unsigned chunks = (unsigned)((head_dim / 4 + miattn::kCombineCols - 1) / miattn::kCombineCols);
+  hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3(rows, chunks), dim3(256), 0, (hipStream_t)stream, a);
   const int r = check_launch("combine");
   return r ? r : ok();
 }
@@ -344,7 +345,8 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
     miattn::CombineArgs c;
     c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
     c.rows = (int)rows; c.num_splits = S; c.head_dim = head_dim; c.out_bf16 = 1;
-    hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3((unsigned)rows), dim3(256), 0, st, c);
+    const unsigned chunks = (unsigned)((head_dim / 4 + miattn::kCombineCols - 1) / miattn::kCombineCols);
+    hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3((unsigned)rows, chunks), dim3(256), 0, st, c);
     r = check_launch("combine");
     if (r) return r;
   }

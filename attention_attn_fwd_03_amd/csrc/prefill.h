@@ -31,6 +31,8 @@
 //    them) and the query tiles in decreasing order (heaviest causal tiles
 //    first).
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 namespace miattn {
@@ -131,18 +133,31 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void miattn_prefill_fwd_kern
   const uint16_t* vbase = a.v + (size_t)s0 * kv_row + (size_t)g * D;
 
   u32x4 kreg[SM::PER_THREAD], vreg[SM::PER_THREAD];
+  // Global -> registers for tile kt. Rows past the sequence end (tail tile
+  // only) read the last valid row and are then zeroed, so the loads never
+  // branch and nothing outside the sequence reaches P.V.
   auto fetch = [&](int kt) {
+    const bool full = (kt + 1) * BC <= L;
 #pragma unroll
     for (int it = 0; it < SM::PER_THREAD; ++it) {
       const int id = it * 256 + threadIdx.x;
       const int r = id / (D / 8);
       const int c8 = (id % (D / 8)) * 8;
       const int key = kt * BC + r;
-      u32x4 z = {0u, 0u, 0u, 0u};
-      const bool ok = key < L;
-      const size_t off = (size_t)(ok ? key : 0) * kv_row + c8;
-      kreg[it] = ok ? ld16(kbase + off) : z;
-      vreg[it] = ok ? ld16(vbase + off) : z;
+      const int krow = full ? key : (key < L ? key : L - 1);
+      const size_t off = (size_t)krow * kv_row + c8;
+      kreg[it] = ld16(kbase + off);
+      vreg[it] = ld16(vbase + off);
+    }
+    if (!full) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int it = 0; it < SM::PER_THREAD; ++it) {
+        const int id = it * 256 + threadIdx.x;
+        const bool bad = kt * BC + id / (D / 8) >= L;
+        kreg[it] = bad ? z : kreg[it];
+        vreg[it] = bad ? z : vreg[it];
+      }
     }
   };
   auto stash = [&](int buf) {
@@ -166,6 +181,79 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void miattn_prefill_fwd_kern
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
 
+  const float c = a.c;
+  const int bb = lane >> 4, kq = lane & 15;
+  // per-lane LDS offsets (elements) of the K operand rows and the V^T reads
+  const int k_off = (lane & 31) * SM::KROW + 8 * half;
+  const int v_off = (4 * (bb >> 1) + (kq >> 2)) * SM::VROW + 16 * (bb & 1) + 4 * (kq & 3);
+
+  // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
+  auto tile = [&](int kt, int buf, bool need_mask) {
+    const MIATTN_LDS uint16_t* kl = (const MIATTN_LDS uint16_t*)(smem + buf * SM::STAGE) + k_off;
+    const MIATTN_LDS uint16_t* vl = (const MIATTN_LDS uint16_t*)(smem + buf * SM::STAGE + SM::KBYTES) + v_off;
+    f32x16 s[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            as_bf16x8(lds_ld16(kl + 32 * kb * SM::KROW + 16 * kk)), as_bf16x8(qop[kk]), s[kb], 0, 0, 0);
+    }
+    if (need_mask) {   // diagonal or tail tile only (uniform branch)
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt * BC + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool ok = key < L && (!CAUSAL || key <= qrow);
+          s[kb][r] = ok ? s[kb][r] : kNegInf;
+        }
+    }
+    // raw-score row max (scale > 0, so max(s * c) = c * max(s))
+    float smax = kNegInf;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) smax = fmaxf(smax, s[kb][r]);
+    smax = fmaxf(smax, xor32(smax));
+    const float tmax = smax * c;
+    if (__builtin_amdgcn_ballot_w64(tmax > m + kFwdRescaleThreshold)) {
+      const float mn = fmaxf(m, tmax);
+      const float alpha = (m == kNegInf) ? 0.f : exp2_hw(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+      m = mn;
+    }
+    const float nmu = (m == kNegInf) ? 0.f : -m;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      uint32_t pw[8];
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, nmu));
+        const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, nmu));
+        l += p0 + p1;
+        pw[r >> 1] = pack_bf16x2(p0, p1);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const u32x4 pu = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
+        const bf16x8 pop = as_bf16x8(pu);
+        // V^T rows: keys 32kb + 16u + 4(lane/32) + {0..3} and the same + 8
+        const MIATTN_LDS uint16_t* vp = vl + (32 * kb + 16 * u) * SM::VROW;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const u32x2 lo = lds_ld_tr16(vp + 32 * dt);
+          const u32x2 hi = lds_ld_tr16(vp + 8 * SM::VROW + 32 * dt);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lo, hi), pop, acc[dt], 0, 0, 0);
+        }
+      }
+    }
+  };
+
   fetch(0);
   stash(0);
   __syncthreads();
@@ -174,72 +262,7 @@ __global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void miattn_prefill_fwd_kern
     const int buf = kt & 1;
     if (kt + 1 < n_kt) fetch(kt + 1);
     if (kt < n_kt_w) {
-      const MIATTN_LDS uint16_t* kl = (const MIATTN_LDS uint16_t*)(smem + buf * SM::STAGE);
-      const MIATTN_LDS uint16_t* vl = (const MIATTN_LDS uint16_t*)(smem + buf * SM::STAGE + SM::KBYTES);
-      // S^T blocks: keys 32kb + 8(r/4) + 4 half + r%4, query row qrow
-      f32x16 s[KB];
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-        const MIATTN_LDS uint16_t* kp = kl + (32 * kb + (lane & 31)) * SM::KROW + 8 * half;
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk)
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lds_ld16(kp + 16 * kk)),
-                                                          as_bf16x8(qop[kk]), s[kb], 0, 0, 0);
-      }
-      // scale into log2 units, mask, tile row max
-      const bool need_mask = (kt + 1) * BC > L || (CAUSAL && (kt + 1) * BC - 1 > wq_lo);
-      float tmax = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float t = s[kb][r] * a.c;
-          if (need_mask) {
-            const int key = kt * BC + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = key < L && (!CAUSAL || key <= qrow);
-            t = ok ? t : kNegInf;
-          }
-          s[kb][r] = t;
-          tmax = fmaxf(tmax, t);
-        }
-      tmax = fmaxf(tmax, xor32(tmax));
-      if (__builtin_amdgcn_ballot_w64(tmax > m + kFwdRescaleThreshold)) {
-        const float mn = fmaxf(m, tmax);
-        const float alpha = (m == kNegInf) ? 0.f : exp2_hw(m - mn);
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-        m = mn;
-      }
-      const float mu = (m == kNegInf) ? 0.f : m;
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        uint32_t pw[8];
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2_hw(s[kb][r] - mu);
-          const float p1 = exp2_hw(s[kb][r + 1] - mu);
-          l += p0 + p1;
-          pw[r >> 1] = pack_bf16x2(p0, p1);
-        }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-          const u32x4 pu = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
-          const bf16x8 pop = as_bf16x8(pu);
-          // V^T operand rows: keys 32kb + 16u + 4 half + {0..3} and +8
-          const int bb = lane >> 4, kq = lane & 15;
-          const MIATTN_LDS uint16_t* vp =
-              vl + (32 * kb + 16 * u + 4 * (bb >> 1) + (kq >> 2)) * SM::VROW + 16 * (bb & 1) + 4 * (kq & 3);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const u32x2 lo = lds_ld_tr16(vp + 32 * dt);
-            const u32x2 hi = lds_ld_tr16(vp + 8 * SM::VROW + 32 * dt);
-            acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lo, hi), pop, acc[dt], 0, 0, 0);
-          }
-        }
-      }
+      tile(kt, buf, (kt + 1) * BC > L || (CAUSAL && (kt + 1) * BC - 1 > wq_lo));
     }
     if (kt + 1 < n_kt) stash(buf ^ 1);
     __syncthreads();

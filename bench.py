@@ -92,6 +92,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = library policy")
     ap.add_argument("--long-splits", type=int, default=0, help="0 = library policy")
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "copy"], default=None,
+                    help="profiling aid: run just one stage (or a 1 GiB device copy used to calibrate "
+                         "the HBM byte counters) for --steps iterations and print its mean time")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
@@ -110,6 +113,22 @@ def main():
 
     def i32(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / args.steps
+        print(json.dumps({"only": "copy", "bytes_read": n, "bytes_written": n, "ms": dt * 1e3,
+                          "GB/s": 2 * n / dt / 1e9}), flush=True)
+        return
 
     print("[bench] generating inputs", file=sys.stderr, flush=True)
     pc = synth.config2(S=4096, seed=0)
@@ -141,6 +160,20 @@ def main():
                              num_splits=lsplits, out=Ld["o"], lse=Ld["lse"])
 
     stages = [prefill, decode, long_decode]
+    if args.only is not None:
+        f = {"prefill": prefill, "decode": decode, "long": long_decode}[args.only]
+        for _ in range(args.warmup):
+            f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            f()
+        e1.record()
+        torch.cuda.synchronize()
+        print(json.dumps({"only": args.only, "ms": e0.elapsed_time(e1) / args.steps}), flush=True)
+        return
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):
         for f in stages:
