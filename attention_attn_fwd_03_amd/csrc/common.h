@@ -55,6 +55,10 @@ __device__ __forceinline__ int lane_id() {
 // 16-byte global load / store through plain vector types.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Non-temporal 16-byte load for data that is read exactly once.
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ u32x4 lds_ld16(const MIATTN_LDS void* p) {
   return *reinterpret_cast<const MIATTN_LDS u32x4*>(p);
 }

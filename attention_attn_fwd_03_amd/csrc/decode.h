@@ -7,11 +7,20 @@
 // LLM feels dumber than it is", section "Why the calculation is split into
 // groups"), merged afterwards by the combine kernel.
 //
-// Work decomposition: one workgroup of 4 waves per (split, kv head, sequence).
-// The G = Hq/Hkv query heads that share a kv head are served together, so each
-// K/V byte is read from HBM once. Inside the split, wave w takes pages w, w+4,
-// ..., keeps its own running max / sum / output, and the four waves are merged
-// through LDS in a fixed order at the end.
+// Split plan: split s of a sequence covers pages [s P, (s+1) P) of it, with
+// P = ceil(max_pages / num_splits) from the block-table width; a sequence
+// shorter than the table leaves its trailing splits empty (merged as (0, -inf)).
+// For one sequence that fills the table this is the contiguous equal-count
+// partition of the pages.
+//
+// Work decomposition: one workgroup of 8 waves per (group of HW kv heads,
+// sequence, split), HW = 8, 4, 2 or 1, with 8/HW waves per kv head taking the
+// split's pages in turn. With HW = Hkv a workgroup reads every kv head of a
+// page together, i.e. whole 16-token pages as contiguous runs of token rows,
+// instead of one head's slice of each row. The G = Hq/Hkv query heads that
+// share a kv head are served together, so each K/V byte is read from HBM once.
+// Each wave keeps its own running max / sum / output; the waves of a kv head
+// are merged through LDS in a fixed order at the end.
 //
 // Per page (16 tokens) a wave computes S^T = K . Q^T with 16x16x32 bf16 MFMAs
 // (rows: tokens, columns: query heads, padded to 16), so lane l holds query
@@ -34,16 +43,19 @@ struct DecodeArgs {
   float* part_lse;              // [B*Hq, S] fp32
   uint16_t* o;                  // [B, Hq, D] bf16     (num_splits == 1)
   float* lse;                   // [B, Hq] fp32 or null
+  int batch;
   int max_pages;
   int num_pages;
   int num_q_heads;
   int num_kv_heads;
   int group;                    // G = Hq / Hkv (<= 8)
+  int heads_per_wg;             // HW: kv heads served by one workgroup (8, 4, 2 or 1)
   int num_splits;
   float c;                      // scale * log2(e)
 };
 
-constexpr int kDecodeWaves = 4;
+constexpr int kDecodeWaves = 8;
+constexpr int kDecodeThreads = 64 * kDecodeWaves;
 constexpr int kDecodeMaxGroup = 8;
 constexpr int kPage = 16;
 // Lazy rescaling: the running max only moves when a page's max exceeds it by
@@ -59,18 +71,34 @@ struct DecodeSmem {
                                 + 2 * kDecodeWaves * 16 * 4;      // m and l per wave and head
 };
 
+// PF = pages each wave keeps in flight (register double buffering when 2).
 template <int D>
-__global__ __launch_bounds__(256) void miattn_decode_split_kernel(DecodeArgs a) {
+constexpr int decode_prefetch() { return D >= 256 ? 1 : 2; }
+
+template <int D>
+__global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(DecodeArgs a) {
   constexpr int NKK = D / 32;   // 16x16x32 steps over the head dim, one 16-B chunk each
   constexpr int NDT = D / 16;   // 16-wide d tiles of the output
+  constexpr int PF = decode_prefetch<D>();
   using Smem = DecodeSmem<D>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[Smem::kBytes];
 
-  const int split = blockIdx.x;
-  const int g = blockIdx.y;
-  const int b = blockIdx.z;
+  // 1-D grid: head group fastest, then sequence, split slowest. Workgroups are
+  // dealt to the XCDs round robin, so every XCD gets a balanced mix of
+  // sequences and split indices, and the (mostly empty) high split indices
+  // come last.
+  const int HW = a.heads_per_wg;
+  const int WPH = kDecodeWaves / HW;                 // waves per kv head
+  const int n_hg = a.num_kv_heads / HW;
+  const int lin = blockIdx.x;
+  const int per_split = n_hg * a.batch;
+  const int split = lin / per_split;
+  const int hg = (lin % per_split) % n_hg;
+  const int b = (lin % per_split) / n_hg;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = hg * HW + wave / WPH;                // this wave's kv head
+  const int phase = wave % WPH;                      // this wave's pages: phase + WPH i
   const int tok = lane & 15;     // token row for K/V loads and the S^T A operand
   const int quad = lane >> 4;    // 0..3
   const int hl = lane & 15;      // query head (within the group) owned by this lane
@@ -80,12 +108,12 @@ __global__ __launch_bounds__(256) void miattn_decode_split_kernel(DecodeArgs a) 
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
   const int n_pages = (L + kPage - 1) / kPage;
-  const int pps = (n_pages + a.num_splits - 1) / a.num_splits;
+  // every split of every sequence covers the same page budget, sized from the
+  // block-table width, so sequences of different lengths balance
+  const int pps = (a.max_pages + a.num_splits - 1) / a.num_splits;
   const int p0 = split * pps < n_pages ? split * pps : n_pages;
   const int p1 = p0 + pps < n_pages ? p0 + pps : n_pages;
-  // pages p0 + wave + 4*i, i < np
-  const int np = (p1 - p0 - wave + kDecodeWaves - 1) / kDecodeWaves > 0
-                     ? (p1 - p0 - wave + kDecodeWaves - 1) / kDecodeWaves : 0;
+  const int np = (p1 - p0 - phase + WPH - 1) / WPH > 0 ? (p1 - p0 - phase + WPH - 1) / WPH : 0;
 
   // Q^T operand: head hl, d = 32*kk + 8*quad .. +7 (zero for padding heads).
   u32x4 qop[NKK];
@@ -101,7 +129,21 @@ __global__ __launch_bounds__(256) void miattn_decode_split_kernel(DecodeArgs a) 
 
   const size_t row_stride = (size_t)Hkv * D;               // elements between tokens
   const size_t page_stride = (size_t)kPage * row_stride;   // elements between pages
-  const int32_t* bt = a.block_table + (size_t)b * a.max_pages;
+  const int32_t* bt = a.block_table + (size_t)b * a.max_pages + p0 + phase;
+
+  // Block-table entries of the wave's pages, 64 at a time: lane j holds page
+  // j of the current window (-1 if out of range or invalid).
+  int bt_win = -1;
+  auto load_bt_window = [&](int first) {
+    const int i = first + lane;
+    int pp = -1;
+    if (i < np) {
+      pp = bt[WPH * i];
+      pp = (pp >= 0 && pp < a.num_pages) ? pp : -1;
+    }
+    bt_win = pp;
+  };
+  auto phys_page = [&](int i) -> int { return __builtin_amdgcn_readlane(bt_win, i & 63); };
 
   float m = kNegInf;   // running max (log2 units) for head hl
   float l = 0.f;       // partial running sum over this lane's tokens
@@ -111,39 +153,41 @@ __global__ __launch_bounds__(256) void miattn_decode_split_kernel(DecodeArgs a) 
 
   MIATTN_LDS uint16_t* vstage = (MIATTN_LDS uint16_t*)(smem) + wave * kPage * Smem::kRowElems;
 
-  // Physical page of the wave's i-th page, or -1 when out of range.
-  auto phys_page = [&](int i) -> int {
-    int pp = bt[p0 + wave + kDecodeWaves * i];
-    return (pp >= 0 && pp < a.num_pages) ? pp : -1;
-  };
-  // Token slot `tok` of logical page lp is a real token?
-  auto load_page = [&](int i, u32x4* kb, u32x4* vb) {
-    const int lp = p0 + wave + kDecodeWaves * i;
+  // K/V rows of the wave's i-th page (token `tok`, this lane's d chunks);
+  // returns the physical page (-1: contributes nothing). The page must lie in
+  // the current block-table window. Loads never branch: an invalid page reads
+  // page 0 and its values are masked (K) or zeroed (V) before use.
+  auto load_page = [&](int i, u32x4* kb, u32x4* vb) -> int {
     const int pp = phys_page(i);
-    const bool ok = pp >= 0 && lp * kPage + tok < L;
-    const uint16_t* kp = a.k_cache + (size_t)(ok ? pp : 0) * page_stride + (size_t)tok * row_stride
+    const uint16_t* kp = a.k_cache + (size_t)(pp >= 0 ? pp : 0) * page_stride + (size_t)tok * row_stride
                          + (size_t)g * D + 8 * quad;
     const uint16_t* vp = a.v_cache + (kp - a.k_cache);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      kb[kk] = ok ? ld16(kp + 32 * kk) : z;
-      vb[kk] = ok ? ld16(vp + 32 * kk) : z;
+      kb[kk] = ld16(kp + 32 * kk);
+      vb[kk] = ld16(vp + 32 * kk);
     }
+    return pp;
   };
 
-  auto process = [&](int i, const u32x4* kb, const u32x4* vb) {
-    const int lp = p0 + wave + kDecodeWaves * i;
-    const bool page_ok = phys_page(i) >= 0;
-    // S^T = K . Q^T  (16 tokens x 16 heads)
+  // Page i: S^T = K Q^T, stage V in LDS (rows of tokens past the sequence end
+  // or of an invalid page as zeros); the caller may then refill kb/vb.
+  auto scores = [&](int i, bool page_ok, const u32x4* kb, const u32x4* vb) -> f32x4 {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[kk]), as_bf16x8(qop[kk]), s, 0, 0, 0);
-    // stage V for the transposing reads (tokens x d, padded rows)
+    const int lp = p0 + phase + WPH * i;
+    const bool row_ok = page_ok && lp * kPage + tok < L;
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      lds_st16(vstage + tok * Smem::kRowElems + 32 * kk + 8 * quad, vb[kk]);
+      lds_st16(vstage + tok * Smem::kRowElems + 32 * kk + 8 * quad, row_ok ? vb[kk] : z);
+    return s;
+  };
+  // Online softmax for page i and O^T += V^T P^T from the staged V.
+  auto accumulate = [&](int i, f32x4 s, bool page_ok) {
+    const int lp = p0 + phase + WPH * i;
     float t[4];
     float pm = kNegInf;
 #pragma unroll
@@ -169,7 +213,6 @@ __global__ __launch_bounds__(256) void miattn_decode_split_kernel(DecodeArgs a) 
     l += (p[0] + p[1]) + (p[2] + p[3]);
     u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
     const bf16x4 pop = as_bf16x4(pw);
-    // O^T += V^T . P^T, one 16x16x16 MFMA per 16-wide d tile
     const MIATTN_LDS uint16_t* vt = vstage + (4 * quad + (tok >> 2)) * Smem::kRowElems + 4 * (tok & 3);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
@@ -178,16 +221,28 @@ __global__ __launch_bounds__(256) void miattn_decode_split_kernel(DecodeArgs a) 
     }
   };
 
-  {
-    u32x4 kb0[NKK], vb0[NKK], kb1[NKK], vb1[NKK];
-    if (np > 0) load_page(0, kb0, vb0);
-    if (np > 1) load_page(1, kb1, vb1);
-    for (int i = 0; i < np; i += 2) {
-      process(i, kb0, vb0);
-      if (i + 2 < np) load_page(i + 2, kb0, vb0);
-      if (i + 1 < np) {
-        process(i + 1, kb1, vb1);
-        if (i + 3 < np) load_page(i + 3, kb1, vb1);
+  // Pages are walked in windows of 64 (one block-table entry per lane).
+  // Inside a window every load is unconditional: the prefetch past the last
+  // page re-reads that page and a uniform branch skips its accumulation, so
+  // the compiler can count outstanding loads exactly and wait only for the
+  // page about to be used.
+  for (int w0 = 0; w0 < np; w0 += 64) {
+    const int n_in = np - w0 < 64 ? np - w0 : 64;
+    load_bt_window(w0);
+    u32x4 kb[PF][NKK], vb[PF][NKK];
+    int pp_buf[PF];
+#pragma unroll
+    for (int j = 0; j < PF; ++j) pp_buf[j] = load_page(w0 + (j < n_in ? j : n_in - 1), kb[j], vb[j]);
+    for (int i0 = 0; i0 < n_in; i0 += PF) {
+#pragma unroll
+      for (int j = 0; j < PF; ++j) {
+        const int ii = i0 + j;                  // index inside the window
+        const bool live = ii < n_in;            // uniform
+        const bool ok_i = live && pp_buf[j] >= 0;
+        const f32x4 s = scores(w0 + ii, ok_i, kb[j], vb[j]);
+        const int nxt = ii + PF < n_in ? ii + PF : n_in - 1;
+        pp_buf[j] = load_page(w0 + nxt, kb[j], vb[j]);
+        if (live) accumulate(w0 + ii, s, ok_i);
       }
     }
   }
@@ -211,17 +266,19 @@ __global__ __launch_bounds__(256) void miattn_decode_split_kernel(DecodeArgs a) 
   }
   __syncthreads();
 
+  // merge the WPH waves of each kv head in wave order; one output row per
+  // (kv head, query head in its group)
   const int S = a.num_splits;
-  for (int idx = threadIdx.x; idx < G * (D / 4); idx += 256) {
-    const int h = idx / (D / 4);
+  for (int idx = threadIdx.x; idx < HW * G * (D / 4); idx += kDecodeThreads) {
+    const int gh = idx / (G * (D / 4));           // kv head within the workgroup
+    const int h = (idx / (D / 4)) % G;
     const int d4 = (idx % (D / 4)) * 4;
+    const int w0 = gh * WPH;
     float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) M = fmaxf(M, mm[w * 16 + h]);
+    for (int w = w0; w < w0 + WPH; ++w) M = fmaxf(M, mm[w * 16 + h]);
     float Lsum = 0.f;
     f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int w = 0; w < kDecodeWaves; ++w) {
+    for (int w = w0; w < w0 + WPH; ++w) {
       const float mw = mm[w * 16 + h];
       const float f = (mw == kNegInf) ? 0.f : exp2_hw(mw - M);
       Lsum += f * ml[w * 16 + h];
@@ -231,7 +288,7 @@ __global__ __launch_bounds__(256) void miattn_decode_split_kernel(DecodeArgs a) 
     const float inv = empty ? 0.f : 1.f / Lsum;
     o *= inv;
     const float lse = empty ? kNegInf : (M + log2_hw(Lsum)) * kLn2;
-    const size_t row = (size_t)b * a.num_q_heads + (size_t)g * G + h;
+    const size_t row = (size_t)b * a.num_q_heads + (size_t)(hg * HW + gh) * G + h;
     if (S == 1) {
       u32x2 w2 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
       *reinterpret_cast<u32x2*>(a.o + row * D + d4) = w2;

@@ -73,25 +73,35 @@ int check_launch(const char* what) {
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 // --- prefill launches ------------------------------------------------------
-template <int D, int KB, bool CAUSAL>
+template <int D, int QB, int KB, bool CAUSAL>
 void launch_fwd(const miattn::FwdArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((miattn::miattn_prefill_fwd_kernel<D, KB, CAUSAL>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((miattn::miattn_prefill_fwd_kernel<D, QB, KB, CAUSAL>), dim3(grid), dim3(256), 0, st, a);
 }
 
-template <int D, int KB>
+template <int D, int QB, int KB>
 void launch_fwd_c(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t st) {
-  if (causal) launch_fwd<D, KB, true>(a, grid, st);
-  else launch_fwd<D, KB, false>(a, grid, st);
+  if (causal) launch_fwd<D, QB, KB, true>(a, grid, st);
+  else launch_fwd<D, QB, KB, false>(a, grid, st);
 }
+
+// query blocks of 32 rows per wave for each head_dim
+constexpr int fwd_qb(int d) { return d >= 256 ? 1 : 1; }
 
 template <int D>
-void launch_decode(const miattn::DecodeArgs& a, int batch, hipStream_t st) {
-  hipLaunchKernelGGL((miattn::miattn_decode_split_kernel<D>), dim3(a.num_splits, a.num_kv_heads, batch),
-                     dim3(256), 0, st, a);
+void launch_decode(const miattn::DecodeArgs& a, hipStream_t st) {
+  const unsigned grid = (unsigned)((long)a.num_splits * (a.num_kv_heads / a.heads_per_wg) * a.batch);
+  hipLaunchKernelGGL((miattn::miattn_decode_split_kernel<D>), dim3(grid), dim3(miattn::kDecodeThreads), 0, st, a);
+}
+
+// kv heads per decode workgroup: the largest of 8, 4, 2, 1 dividing Hkv
+int decode_heads_per_wg(int hkv) {
+  for (int h = 8; h > 1; h >>= 1)
+    if (hkv % h == 0) return h;
+  return 1;
 }
 
 int split_rule(long total_tokens, long work_units, long cu_count, long wg_per_cu, long block_tokens,
-               long max_splits) {
+               long max_splits, double threshold) {
   if (total_tokens <= 0 || work_units <= 0 || cu_count <= 0 || wg_per_cu <= 0 || block_tokens <= 0 ||
       max_splits <= 0)
     return MIATTN_ERR_INVALID_ARG;
@@ -109,7 +119,7 @@ int split_rule(long total_tokens, long work_units, long cu_count, long wg_per_cu
       const double eff = ratio / std::ceil(ratio);
       if (pass == 0) {
         if (eff > best) best = eff;
-      } else if (eff >= 0.85 * best) {
+      } else if (eff >= threshold * best) {
         return (int)s;
       }
     }
@@ -117,11 +127,16 @@ int split_rule(long total_tokens, long work_units, long cu_count, long wg_per_cu
   return 1;
 }
 
-// MI355X decode capacity: 256 compute units, two split workgroups resident per
-// unit, splits counted in 16-token pages, at most 256 splits.
+// MI355X decode capacity: 256 compute units, one 8-wave split workgroup
+// resident per unit, splits counted in 16-token pages, at most 256 splits. The
+// decode is HBM-bound and its combine is cheap, so the policy takes the
+// smallest split count with the best efficiency (the pages' rule settles for
+// 85% of it to save merge work).
 constexpr int kCUs = 256;
-constexpr int kDecodeWgPerCu = 2;
+constexpr int kDecodeWgPerCu = 1;
 constexpr int kMaxSplits = 256;
+constexpr double kPagesRuleThreshold = 0.85;
+constexpr double kDecodePolicyThreshold = 1.0;
 
 }  // namespace
 
@@ -161,15 +176,16 @@ void miattn_release(void) {
 
 int miattn_split_heuristic(int total_tokens, int work_units, int cu_count, int wg_per_cu, int block_tokens,
                            int max_splits) {
-  const int r = split_rule(total_tokens, work_units, cu_count, wg_per_cu, block_tokens, max_splits);
+  const int r = split_rule(total_tokens, work_units, cu_count, wg_per_cu, block_tokens, max_splits,
+                           kPagesRuleThreshold);
   if (r < 0) return fail(r, "split heuristic: all arguments must be positive");
   return r;
 }
 
 int miattn_decode_pick_splits(int batch, int num_kv_heads, int max_seq_len) {
   if (batch <= 0 || num_kv_heads <= 0 || max_seq_len <= 0) return 1;
-  return split_rule(max_seq_len, (long)batch * num_kv_heads, kCUs, kDecodeWgPerCu, MIATTN_PAGE_SIZE,
-                    kMaxSplits);
+  const long work = (long)batch * (num_kv_heads / decode_heads_per_wg(num_kv_heads));
+  return split_rule(max_seq_len, work, kCUs, kDecodeWgPerCu, MIATTN_PAGE_SIZE, kMaxSplits, kDecodePolicyThreshold);
 }
 
 size_t miattn_decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int num_splits) {
@@ -231,17 +247,18 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
   a.num_seqs = num_seqs; a.total_tokens = total_tokens;
   a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
   a.heads_per_wg = G >= 4 ? 4 : G;
-  const int QR = 32 * (4 / a.heads_per_wg);
-  a.n_qtiles = (max_seqlen + QR - 1) / QR;
+  const int QR = 32 * fwd_qb(head_dim) * (4 / a.heads_per_wg);
+  const int n_qtiles = (max_seqlen + QR - 1) / QR;
+  a.n_pairs = (n_qtiles + 1) / 2;
   a.n_head_slots = num_kv_heads * (G / a.heads_per_wg);
   a.c = c;
-  const long grid = (long)a.n_head_slots * num_seqs * a.n_qtiles;
+  const long grid = (long)a.n_head_slots * num_seqs * a.n_pairs;
   if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: problem too large");
   const bool cz = causal != 0;
   switch (head_dim) {
-    case 64: launch_fwd_c<64, 2>(a, (int)grid, cz, st); break;
-    case 128: launch_fwd_c<128, 2>(a, (int)grid, cz, st); break;
-    default: launch_fwd_c<256, 1>(a, (int)grid, cz, st); break;
+    case 64: launch_fwd_c<64, fwd_qb(64), 2>(a, (int)grid, cz, st); break;
+    case 128: launch_fwd_c<128, fwd_qb(128), 2>(a, (int)grid, cz, st); break;
+    default: launch_fwd_c<256, fwd_qb(256), 1>(a, (int)grid, cz, st); break;
   }
   const int r = check_launch("prefill bf16");
   return r ? r : ok();
@@ -289,12 +306,12 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
   if (head_dim != 64 && head_dim != 128 && head_dim != 256)
     return fail(MIATTN_ERR_UNSUPPORTED, "attn_decode_paged: head_dim must be 64, 128 or 256");
   if (!scale_ok(scale)) return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: scale must be finite and > 0");
-  if (batch > 65535 || num_kv_heads > 65535)
-    return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: batch and Hkv must be <= 65535");
   int S = num_splits;
   if (S == 0) S = miattn_decode_pick_splits(batch, num_kv_heads, max_pages_per_seq * MIATTN_PAGE_SIZE);
   if (S > max_pages_per_seq) S = max_pages_per_seq;   // more splits than pages would only add empty groups
   if (S < 1) S = 1;
+  if ((long)S * num_kv_heads * batch > 0x7fffffffL)
+    return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: splits * Hkv * batch too large");
   const size_t need = miattn_decode_workspace_bytes(batch, num_q_heads, head_dim, S);
   if (workspace != nullptr && workspace_bytes < need)
     return fail(MIATTN_ERR_WORKSPACE, "attn_decode_paged: workspace of %zu bytes, need %zu", workspace_bytes,
@@ -326,18 +343,19 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
   }
   miattn::DecodeArgs a;
   a.q = (const uint16_t*)q; a.k_cache = (const uint16_t*)k_cache; a.v_cache = (const uint16_t*)v_cache;
-  a.block_table = block_table; a.seq_lens = seq_lens;
+  a.block_table = block_table; a.seq_lens = seq_lens; a.batch = batch;
   const size_t rows = (size_t)batch * num_q_heads;
   a.part_o = S > 1 ? (float*)ws : nullptr;
   a.part_lse = S > 1 ? (float*)ws + rows * (size_t)S * head_dim : nullptr;
   a.o = (uint16_t*)o; a.lse = lse;
   a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
   a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = num_q_heads / num_kv_heads;
+  a.heads_per_wg = decode_heads_per_wg(num_kv_heads);
   a.num_splits = S; a.c = scale * miattn::kLog2e;
   switch (head_dim) {
-    case 64: launch_decode<64>(a, batch, st); break;
-    case 128: launch_decode<128>(a, batch, st); break;
-    default: launch_decode<256>(a, batch, st); break;
+    case 64: launch_decode<64>(a, st); break;
+    case 128: launch_decode<128>(a, st); break;
+    default: launch_decode<256>(a, st); break;
   }
   int r = check_launch("decode split");
   if (r) return r;

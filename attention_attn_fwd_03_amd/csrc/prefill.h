@@ -7,13 +7,19 @@
 // P V accumulates into registers, and O / l is cast to bf16 at the end.
 //
 // MI355X mapping:
-//  * Workgroup = 4 waves. Waves split the NH query heads of one kv-head group
-//    (NH = min(G, 4)) and 4/NH blocks of 32 query rows, so every wave reuses
-//    the same K/V tile from LDS (GQA sharing of "GPU Datapath", section C).
-//  * K/V tiles of Bc = 32*KB keys are double-buffered in LDS. The next tile is
-//    fetched into registers with coalesced 16-byte loads while the current
-//    tile is consumed, then written to the other LDS buffer; one barrier per
-//    tile.
+//  * Workgroup = 4 waves, one per SIMD. Waves split the NH query heads of one
+//    kv-head group (NH = min(G, 4)) and 4/NH row ranges; each wave owns QB
+//    blocks of 32 query rows (64 rows for head_dim <= 128), so every K and V
+//    operand read from LDS feeds QB MFMAs (LDS bytes per flop halve at QB=2)
+//    and all waves reuse the same K/V tile (GQA sharing of "GPU Datapath",
+//    section C).
+//  * K/V tiles of Bc = 32*KB keys are double-buffered in LDS. Tiles are
+//    fetched into registers with coalesced 16-byte loads (K two tiles ahead,
+//    V one ahead) and written to LDS at the end of the iteration; one barrier
+//    per tile.
+//  * Software pipeline inside each wave: while the vector ALUs turn tile j's
+//    scores into probabilities, the matrix cores already compute tile j+1's
+//    scores, then consume tile j's probabilities in P.V.
 //  * S^T = K . Q^T on 32x32x16 bf16 MFMAs: lane l owns query row l%32 and 16
 //    of every 32 keys (the other 16 sit in lane l^32), so row max and row sum
 //    are in-lane reductions plus one v_permlane32_swap.
@@ -25,11 +31,11 @@
 //    S^T, rounded to bf16, are already the B operand; V^T comes from LDS
 //    through ds_read_b64_tr_b16. Lane l then holds all of query row l%32's
 //    output columns it owns, so the rescale is a per-lane scalar multiply.
-//  * Grid: one workgroup per (kv-head group, query tile, sequence), with the
-//    head index varying fastest (workgroups are dealt to the 8 XCDs round
-//    robin, so a kv head's K/V stays in one XCD's L2 when there are 8 of
-//    them) and the query tiles in decreasing order (heaviest causal tiles
-//    first).
+//  * Grid: one workgroup per (kv-head group, query-tile pair, sequence); a
+//    workgroup takes query tiles i and n-1-i of its sequence, so every causal
+//    workgroup does the same work. The head index varies fastest: workgroups
+//    are dealt to the 8 XCDs round robin, so with 8 kv heads each XCD's L2
+//    serves one head's K/V.
 #pragma once
 #include <type_traits>
 
@@ -50,241 +56,300 @@ struct FwdArgs {
   int num_kv_heads;
   int group;                  // G
   int heads_per_wg;           // NH
-  int n_qtiles;               // query tiles per sequence (ceil(max_seqlen / QR))
+  int n_pairs;                // query-tile pairs per sequence (ceil(ceil(max_seqlen / QR) / 2))
   int n_head_slots;           // Hkv * G / NH
   float c;                    // scale * log2(e)
 };
 
 constexpr float kFwdRescaleThreshold = 8.0f;
 
+// LDS tile of BC rows x D bf16, stored unpadded as 16-byte slots; chunk c of
+// row r sits in slot c ^ swz(r). K uses swz = r mod 16 (the 128-bit operand
+// reads of 16 consecutive rows hit 16 different bank groups); V uses
+// 2 (r mod 8) + bit 3 of r (the transposing reads of 4 consecutive rows x 2
+// chunks hit 8 different bank groups). Tiles are filled by direct global->LDS
+// loads of whole rows (16 lanes x 16 B per row), so global reads stay
+// row-contiguous.
 template <int D, int KB>
-struct FwdSmem {
+struct FwdTile {
   static constexpr int BC = 32 * KB;
-  static constexpr int KROW = D + 8;     // bf16 elements per K row in LDS (16-B pad)
-  static constexpr int VROW = D + 32;    // bf16 elements per V row in LDS (64-B pad)
-  static constexpr int KBYTES = BC * KROW * 2;
-  static constexpr int VBYTES = BC * VROW * 2;
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int BYTES = 2 * STAGE;
-  static constexpr int CHUNKS = BC * D / 8;          // 16-byte chunks per K (or V) tile
-  static constexpr int PER_THREAD = CHUNKS / 256;
-  static_assert(CHUNKS % 256 == 0, "tile must split evenly over 256 threads");
+  static constexpr int CH = D / 8;                      // 16-byte chunks per row
+  static constexpr int SWZ_MASK = (CH < 16 ? CH : 16) - 1;
+  static constexpr int TILE_BYTES = BC * D * 2;
+  static constexpr int NI = TILE_BYTES / 1024 / 4;      // 1-KB direct loads per wave per tile
+  static_assert(TILE_BYTES % 4096 == 0, "tile must split into 1-KB loads over 4 waves");
+  __device__ static int kswz(int r) { return r & SWZ_MASK; }
+  __device__ static int vswz(int r) {
+    return CH >= 16 ? (((r & 7) << 1) | ((r >> 3) & 1)) & SWZ_MASK : (((r & 3) << 1) | ((r >> 2) & 1)) & SWZ_MASK;
+  }
 };
 
-template <int D, int KB, bool CAUSAL>
-__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void miattn_prefill_fwd_kernel(FwdArgs a) {
-  using SM = FwdSmem<D, KB>;
-  constexpr int BC = SM::BC;
+// QB = 32-row query blocks per wave (1 or 2); KB = 32-key blocks per tile.
+template <int D, int QB, int KB, bool CAUSAL>
+__global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_prefill_fwd_kernel(FwdArgs a) {
+  using TL = FwdTile<D, KB>;
+  constexpr int BC = TL::BC;
+  constexpr int CH = TL::CH;
   constexpr int NKK = D / 16;   // MFMA steps over the head dim (16 each)
   constexpr int NDT = D / 32;   // 32-wide output column tiles
-  __shared__ __attribute__((aligned(16))) uint8_t smem[SM::BYTES];
+  // Four distinct LDS objects (K and V, two buffers each): alias analysis can
+  // then tell that a direct load in flight into one buffer does not feed reads
+  // of another, so reads of the current tile need not wait for the prefetch.
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TL::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TL::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TL::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TL::TILE_BYTES];
+  auto kbuf = [&](int i) { return (MIATTN_LDS uint8_t*)(i == 0 ? k_lds0 : k_lds1); };
+  auto vbuf = [&](int i) { return (MIATTN_LDS uint8_t*)(i == 0 ? v_lds0 : v_lds1); };
 
   const int NH = a.heads_per_wg;
   const int WQ = 4 / NH;
-  const int QR = 32 * WQ;
+  const int QR = 32 * QB * WQ;   // query rows per tile
 
-  // --- work item ---------------------------------------------------------
+  // --- work item: (head slot, tile pair, sequence); head slot fastest ------
   const int lin = blockIdx.x;
   const int hslot = lin % a.n_head_slots;
   const int rest = lin / a.n_head_slots;
-  const int qt = a.n_qtiles - 1 - rest / a.num_seqs;
+  const int pair = rest / a.num_seqs;
   const int b = rest % a.num_seqs;
   int s0 = a.cu_seqlens[b];
   int s1 = a.cu_seqlens[b + 1];
   s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
   s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
   const int L = s1 - s0;
-  const int q0 = qt * QR;
-  if (q0 >= L) return;   // uniform over the workgroup
+  const int n_tiles = (L + QR - 1) / QR;
+  // causal tiles i and n-1-i together cost the same for every pair
+  if (pair > n_tiles - 1 - pair) return;   // uniform over the workgroup
+  const int n_mine = (pair == n_tiles - 1 - pair) ? 1 : 2;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hs = wave % NH;
   const int qs = wave / NH;
-  const int gpw = a.group / NH;                 // workgroups per kv head
+  const int gpw = a.group / NH;
   const int g = hslot / gpw;
   const int h = g * a.group + (hslot % gpw) * NH + hs;
-  const int qrow = q0 + 32 * qs + (lane & 31);  // this lane's query position
-  const int half = lane >> 5;                   // 0/1: which 16 of each 32 keys
+  const int half = lane >> 5;
   const int Hq = a.num_q_heads;
   const int Hkv = a.num_kv_heads;
-
-  // --- Q operand (B of S^T = K Q^T): row qrow, d = 16kk + 8 half .. +7 ------
-  u32x4 qop[NKK];
-  {
-    const bool ok = qrow < L;
-    const uint16_t* qp = a.q + ((size_t)(s0 + (ok ? qrow : 0)) * Hq + h) * D + 8 * half;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qop[kk] = ok ? ld16(qp + 16 * kk) : z;
-    }
-  }
-
-  // --- KV extent --------------------------------------------------------
-  const int kend_wg = CAUSAL ? (L < q0 + QR ? L : q0 + QR) : L;
-  const int n_kt = (kend_wg + BC - 1) / BC;
-  const int wq_lo = q0 + 32 * qs;                // first query row of this wave
-  const int kend_w = CAUSAL ? (L < wq_lo + 32 ? L : wq_lo + 32) : L;
-  const int n_kt_w = (kend_w + BC - 1) / BC;     // tiles this wave needs
+  const float c = a.c;
 
   const size_t kv_row = (size_t)Hkv * D;
   const uint16_t* kbase = a.k + (size_t)s0 * kv_row + (size_t)g * D;
   const uint16_t* vbase = a.v + (size_t)s0 * kv_row + (size_t)g * D;
 
-  u32x4 kreg[SM::PER_THREAD], vreg[SM::PER_THREAD];
-  // Global -> registers for tile kt. Rows past the sequence end (tail tile
-  // only) read the last valid row and are then zeroed, so the loads never
-  // branch and nothing outside the sequence reaches P.V.
-  auto fetch = [&](int kt) {
-    const bool full = (kt + 1) * BC <= L;
+  // Direct global -> LDS loads of tile kt into buffer `buf` (K and V). Each
+  // wave issues NI 1-KB loads per tensor; lane i of load j fills slot
+  // lin % CH of row lin / CH (lin = (wave NI + j) 64 + i) with the chunk the
+  // swizzle maps there. The address is a uniform tile base plus a fixed
+  // per-lane 32-bit offset; on the tail tile rows past the sequence end
+  // repeat its last row (their scores are masked, their probabilities 0).
+  uint32_t koff[TL::NI], voff[TL::NI];
 #pragma unroll
-    for (int it = 0; it < SM::PER_THREAD; ++it) {
-      const int id = it * 256 + threadIdx.x;
-      const int r = id / (D / 8);
-      const int c8 = (id % (D / 8)) * 8;
-      const int key = kt * BC + r;
-      const int krow = full ? key : (key < L ? key : L - 1);
-      const size_t off = (size_t)krow * kv_row + c8;
-      kreg[it] = ld16(kbase + off);
-      vreg[it] = ld16(vbase + off);
-    }
-    if (!full) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-#pragma unroll
-      for (int it = 0; it < SM::PER_THREAD; ++it) {
-        const int id = it * 256 + threadIdx.x;
-        const bool bad = kt * BC + id / (D / 8) >= L;
-        kreg[it] = bad ? z : kreg[it];
-        vreg[it] = bad ? z : vreg[it];
-      }
-    }
-  };
-  auto stash = [&](int buf) {
-    MIATTN_LDS uint16_t* kl = (MIATTN_LDS uint16_t*)(smem + buf * SM::STAGE);
-    MIATTN_LDS uint16_t* vl = (MIATTN_LDS uint16_t*)(smem + buf * SM::STAGE + SM::KBYTES);
-#pragma unroll
-    for (int it = 0; it < SM::PER_THREAD; ++it) {
-      const int id = it * 256 + threadIdx.x;
-      const int r = id / (D / 8);
-      const int c8 = (id % (D / 8)) * 8;
-      lds_st16(kl + r * SM::KROW + c8, kreg[it]);
-      lds_st16(vl + r * SM::VROW + c8, vreg[it]);
-    }
-  };
-
-  float m = kNegInf;   // running max of this lane's query row (log2 units)
-  float l = 0.f;       // running sum over the keys this lane holds
-  f32x16 acc[NDT];
-#pragma unroll
-  for (int i = 0; i < NDT; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-
-  const float c = a.c;
-  const int bb = lane >> 4, kq = lane & 15;
-  // per-lane LDS offsets (elements) of the K operand rows and the V^T reads
-  const int k_off = (lane & 31) * SM::KROW + 8 * half;
-  const int v_off = (4 * (bb >> 1) + (kq >> 2)) * SM::VROW + 16 * (bb & 1) + 4 * (kq & 3);
-
-  // One K/V tile: S^T = K Q^T, online softmax, O^T += V^T P^T.
-  auto tile = [&](int kt, int buf, bool need_mask) {
-    const MIATTN_LDS uint16_t* kl = (const MIATTN_LDS uint16_t*)(smem + buf * SM::STAGE) + k_off;
-    const MIATTN_LDS uint16_t* vl = (const MIATTN_LDS uint16_t*)(smem + buf * SM::STAGE + SM::KBYTES) + v_off;
-    f32x16 s[KB];
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            as_bf16x8(lds_ld16(kl + 32 * kb * SM::KROW + 16 * kk)), as_bf16x8(qop[kk]), s[kb], 0, 0, 0);
-    }
-    if (need_mask) {   // diagonal or tail tile only (uniform branch)
-#pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * BC + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool ok = key < L && (!CAUSAL || key <= qrow);
-          s[kb][r] = ok ? s[kb][r] : kNegInf;
-        }
-    }
-    // raw-score row max (scale > 0, so max(s * c) = c * max(s))
-    float smax = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) smax = fmaxf(smax, s[kb][r]);
-    smax = fmaxf(smax, xor32(smax));
-    const float tmax = smax * c;
-    if (__builtin_amdgcn_ballot_w64(tmax > m + kFwdRescaleThreshold)) {
-      const float mn = fmaxf(m, tmax);
-      const float alpha = (m == kNegInf) ? 0.f : exp2_hw(m - mn);
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-      m = mn;
-    }
-    const float nmu = (m == kNegInf) ? 0.f : -m;
-#pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      uint32_t pw[8];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, nmu));
-        const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, nmu));
-        l += p0 + p1;
-        pw[r >> 1] = pack_bf16x2(p0, p1);
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 pu = {pw[4 * u], pw[4 * u + 1], pw[4 * u + 2], pw[4 * u + 3]};
-        const bf16x8 pop = as_bf16x8(pu);
-        // V^T rows: keys 32kb + 16u + 4(lane/32) + {0..3} and the same + 8
-        const MIATTN_LDS uint16_t* vp = vl + (32 * kb + 16 * u) * SM::VROW;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const u32x2 lo = lds_ld_tr16(vp + 32 * dt);
-          const u32x2 hi = lds_ld_tr16(vp + 8 * SM::VROW + 32 * dt);
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lo, hi), pop, acc[dt], 0, 0, 0);
-        }
-      }
-    }
-  };
-
-  fetch(0);
-  stash(0);
-  __syncthreads();
-
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < n_kt) fetch(kt + 1);
-    if (kt < n_kt_w) {
-      tile(kt, buf, (kt + 1) * BC > L || (CAUSAL && (kt + 1) * BC - 1 > wq_lo));
-    }
-    if (kt + 1 < n_kt) stash(buf ^ 1);
-    __syncthreads();
+  for (int j = 0; j < TL::NI; ++j) {
+    const int lidx = (wave * TL::NI + j) * 64 + lane;
+    const int r = lidx / CH;
+    const int slot = lidx % CH;
+    koff[j] = (uint32_t)(((size_t)r * kv_row + 8 * (slot ^ TL::kswz(r))) * 2);
+    voff[j] = (uint32_t)(((size_t)r * kv_row + 8 * (slot ^ TL::vswz(r))) * 2);
   }
-
-  // --- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 ----------------------
-  l += xor32(l);
-  if (qrow < L) {
-    const bool empty = !(l > 0.f);
-    const float inv = empty ? 0.f : 1.f / l;
-    uint16_t* op = a.o + ((size_t)(s0 + qrow) * Hq + h) * D + 4 * half;
+  const uint64_t tile_bytes = (uint64_t)BC * kv_row * 2;
+  auto load_tile = [&](int kt, int buf) {
+    const bool full = (kt + 1) * BC <= L;
+    const char* kb0 = (const char*)kbase + (uint64_t)kt * tile_bytes;
+    const char* vb0 = (const char*)vbase + (uint64_t)kt * tile_bytes;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x16& A = acc[dt];
-        u32x2 w = {pack_bf16x2(A[4 * r4] * inv, A[4 * r4 + 1] * inv),
-                   pack_bf16x2(A[4 * r4 + 2] * inv, A[4 * r4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * r4) = w;
+    for (int j = 0; j < TL::NI; ++j) {
+      uint32_t ko = koff[j], vo = voff[j];
+      if (!full) {
+        const int r = ((wave * TL::NI + j) * 64 + lane) / TL::CH;
+        const int rr = kt * BC + r < L ? r : L - 1 - kt * BC;
+        const uint32_t back = (uint32_t)((size_t)(r - rr) * kv_row * 2);
+        ko -= back;
+        vo -= back;
       }
-    if (a.lse != nullptr && half == 0)
-      a.lse[(size_t)h * a.total_tokens + s0 + qrow] = empty ? kNegInf : (m + log2_hw(l)) * kLn2;
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb0 + ko),
+                                       (MIATTN_LDS void*)(kbuf(buf) + (wave * TL::NI + j) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb0 + vo),
+                                       (MIATTN_LDS void*)(vbuf(buf) + (wave * TL::NI + j) * 1024), 16, 0, 0);
+    }
+  };
+
+  const int bb = lane >> 4, kq = lane & 15;
+
+  for (int tsel = 0; tsel < n_mine; ++tsel) {
+    const int qt = tsel == 0 ? pair : n_tiles - 1 - pair;
+    const int q0 = qt * QR + 32 * QB * qs;   // first query row of this wave
+
+    u32x4 qop[QB][NKK];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = q0 + 32 * qb + (lane & 31);
+      const bool ok = row < L;
+      const uint16_t* qp = a.q + ((size_t)(s0 + (ok ? row : 0)) * Hq + h) * D + 8 * half;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        qop[qb][kk] = ok ? ld16(qp + 16 * kk) : z;
+      }
+    }
+
+    const int qt_end = qt * QR + QR;
+    const int kend_wg = CAUSAL ? (L < qt_end ? L : qt_end) : L;
+    const int n_kt = (kend_wg + BC - 1) / BC;
+    const int kend_w = CAUSAL ? (L < q0 + 32 * QB ? L : q0 + 32 * QB) : L;
+    const int n_kt_w = q0 < L ? (kend_w + BC - 1) / BC : 0;   // tiles this wave computes
+
+    float m[QB], l[QB];
+    f32x16 acc[QB][NDT];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      m[qb] = kNegInf;
+      l[qb] = 0.f;
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[qb][i][r] = 0.f;
+    }
+
+    if (tsel > 0) __syncthreads();   // previous tile's last reads before the buffers are refilled
+    load_tile(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+
+    auto step = [&](int kt, auto bufc) {
+      constexpr int buf = decltype(bufc)::value;
+      if (kt + 1 < n_kt) load_tile(kt + 1, buf ^ 1);
+      if (kt < n_kt_w) {
+        const MIATTN_LDS uint8_t* kl = kbuf(buf);
+        const MIATTN_LDS uint8_t* vl = vbuf(buf);
+        // S^T = K Q^T: lane reads K row 32 kb + lane%32, chunk 2 kk + half
+        f32x16 s[QB][KB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[qb][kb][r] = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          const int r = 32 * kb + (lane & 31);
+          const MIATTN_LDS uint8_t* kr = kl + r * (2 * D);
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            const bf16x8 kop = as_bf16x8(lds_ld16(kr + 16 * ((2 * kk + half) ^ TL::kswz(r))));
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb)
+              s[qb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, as_bf16x8(qop[qb][kk]), s[qb][kb], 0, 0, 0);
+          }
+        }
+        // mask (diagonal / tail tiles only), raw row max, lazy rescale
+        const bool need_mask = (kt + 1) * BC > L || (CAUSAL && (kt + 1) * BC - 1 > q0);
+        if (need_mask) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const int qrow = q0 + 32 * qb + (lane & 31);
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int key = kt * BC + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
+                const bool ok = key < L && (!CAUSAL || key <= qrow);
+                s[qb][kb][r] = ok ? s[qb][kb][r] : kNegInf;
+              }
+          }
+        }
+        float tmax[QB];
+        bool grow = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          float smax = kNegInf;
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) smax = fmaxf(smax, s[qb][kb][r]);
+          smax = fmaxf(smax, xor32(smax));
+          tmax[qb] = smax * c;   // scale > 0, so max(s c) = c max(s)
+          grow = grow || (tmax[qb] > m[qb] + kFwdRescaleThreshold);
+        }
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const float mn = fmaxf(m[qb], tmax[qb]);
+            const float alpha = (m[qb] == kNegInf) ? 0.f : exp2_hw(m[qb] - mn);
+            l[qb] *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc[qb][dt] *= alpha;
+            m[qb] = mn;
+          }
+        }
+        // P = exp2(s c - m), rounded to bf16 for P.V; l sums the fp32 values
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          u32x4 pw[QB][2];
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            const float nmu = (m[qb] == kNegInf) ? 0.f : -m[qb];
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+              const float p0 = exp2_hw(__builtin_fmaf(s[qb][kb][r], c, nmu));
+              const float p1 = exp2_hw(__builtin_fmaf(s[qb][kb][r + 1], c, nmu));
+              l[qb] += p0 + p1;
+              pw[qb][r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
+            }
+          }
+          // O^T += V^T P^T; V^T rows via the transposing read: block bb of
+          // 16 lanes reads keys 32kb + 16u + 4(bb/2) + {0..3} (+8), columns
+          // 32 dt + 16 (bb%2) + {0..15}
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r0 = 32 * kb + 16 * u + 4 * (bb >> 1) + (kq >> 2);
+            const int r1 = r0 + 8;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              const int col = 32 * dt + 16 * (bb & 1) + 4 * (kq & 3);   // element column
+              const int ch = col >> 3, sub = (col & 7) * 2;             // chunk, byte offset in it
+              const u32x2 lo = lds_ld_tr16(vl + r0 * (2 * D) + 16 * (ch ^ TL::vswz(r0)) + sub);
+              const u32x2 hi = lds_ld_tr16(vl + r1 * (2 * D) + 16 * (ch ^ TL::vswz(r1)) + sub);
+              const bf16x8 vop = as_bf16x8(lo, hi);
+#pragma unroll
+              for (int qb = 0; qb < QB; ++qb) {
+                acc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, as_bf16x8(pw[qb][u]), acc[qb][dt], 0, 0, 0);
+              }
+            }
+          }
+        }
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile kt+1 has landed in LDS
+      __syncthreads();
+    };
+    for (int kt = 0; kt < n_kt; kt += 2) {
+      step(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < n_kt) step(kt + 1, std::integral_constant<int, 1>{});
+    }
+
+    // --- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 --------------------
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      float lt = l[qb] + xor32(l[qb]);
+      const int qrow = q0 + 32 * qb + (lane & 31);
+      if (qrow < L) {
+        const bool empty = !(lt > 0.f);
+        const float inv = empty ? 0.f : 1.f / lt;
+        uint16_t* op = a.o + ((size_t)(s0 + qrow) * Hq + h) * D + 4 * half;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x16& A = acc[qb][dt];
+            u32x2 w = {pack_bf16x2(A[4 * r4] * inv, A[4 * r4 + 1] * inv),
+                       pack_bf16x2(A[4 * r4 + 2] * inv, A[4 * r4 + 3] * inv)};
+            *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * r4) = w;
+          }
+        if (a.lse != nullptr && half == 0)
+          a.lse[(size_t)h * a.total_tokens + s0 + qrow] = empty ? kNegInf : (m[qb] + log2_hw(lt)) * kLn2;
+      }
+    }
   }
 }
 

@@ -131,21 +131,27 @@ def main():
         return
 
     print("[bench] generating inputs", file=sys.stderr, flush=True)
+    want = {"prefill", "decode", "long"} if args.only is None else {args.only}
+    P = Dd = Ld = None
     pc = synth.config2(S=4096, seed=0)
-    dc = synth.config3(seed=0, tail="zero")
-    lc = synth.config4(ctx=131072, seed=0)
-
-    P = dict(q=bf16(pc.q), k=bf16(pc.k), v=bf16(pc.v), cu=i32(pc.cu_seqlens))
-    P["o"] = torch.empty_like(P["q"])
-    P["lse"] = torch.empty((pc.num_q_heads, pc.total_tokens), dtype=torch.float32, device=dev)
-    Dd = dict(q=bf16(dc.q), kc=bf16(dc.k_cache), vc=bf16(dc.v_cache), bt=i32(dc.block_table), sl=i32(dc.seq_lens))
-    Dd["o"] = torch.empty_like(Dd["q"])
-    Dd["lse"] = torch.empty((dc.batch, dc.num_q_heads), dtype=torch.float32, device=dev)
-    Ld = dict(q=bf16(lc.q), kc=bf16(lc.k_cache), vc=bf16(lc.v_cache), bt=i32(lc.block_table), sl=i32(lc.seq_lens))
-    Ld["o"] = torch.empty_like(Ld["q"])
-    Ld["lse"] = torch.empty((lc.batch, lc.num_q_heads), dtype=torch.float32, device=dev)
-    dsplits = args.decode_splits or mi.decode_pick_splits(dc.batch, dc.num_kv_heads, dc.max_pages * 16)
-    lsplits = args.long_splits or mi.decode_pick_splits(lc.batch, lc.num_kv_heads, lc.max_pages * 16)
+    if "prefill" in want:
+        P = dict(q=bf16(pc.q), k=bf16(pc.k), v=bf16(pc.v), cu=i32(pc.cu_seqlens))
+        P["o"] = torch.empty_like(P["q"])
+        P["lse"] = torch.empty((pc.num_q_heads, pc.total_tokens), dtype=torch.float32, device=dev)
+    dc = synth.config3(seed=0, tail="zero") if "decode" in want else None
+    if dc is not None:
+        Dd = dict(q=bf16(dc.q), kc=bf16(dc.k_cache), vc=bf16(dc.v_cache), bt=i32(dc.block_table),
+                  sl=i32(dc.seq_lens))
+        Dd["o"] = torch.empty_like(Dd["q"])
+        Dd["lse"] = torch.empty((dc.batch, dc.num_q_heads), dtype=torch.float32, device=dev)
+        dsplits = args.decode_splits or mi.decode_pick_splits(dc.batch, dc.num_kv_heads, dc.max_pages * 16)
+    lc = synth.config4(ctx=131072, seed=0) if "long" in want else None
+    if lc is not None:
+        Ld = dict(q=bf16(lc.q), kc=bf16(lc.k_cache), vc=bf16(lc.v_cache), bt=i32(lc.block_table),
+                  sl=i32(lc.seq_lens))
+        Ld["o"] = torch.empty_like(Ld["q"])
+        Ld["lse"] = torch.empty((lc.batch, lc.num_q_heads), dtype=torch.float32, device=dev)
+        lsplits = args.long_splits or mi.decode_pick_splits(lc.batch, lc.num_kv_heads, lc.max_pages * 16)
 
     def prefill():
         mi.attn_fwd(P["q"], P["k"], P["v"], P["cu"], pc.max_seqlen, scale=pc.scale, causal=True,

@@ -145,9 +145,11 @@ int miattn_attn_combine(const float* partial_o, const float* partial_lse, int ro
  * (0 when num_splits <= 1). */
 size_t miattn_decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int num_splits);
 
-/* Split count chosen for num_splits == 0: the FlashAttention-2-shaped rule
- * of miattn_split_heuristic with this library's MI355X capacity (256 compute
- * units, decode workgroups resident per unit) and 16-token pages as blocks. */
+/* Split count chosen for num_splits == 0: the candidate set and efficiency of
+ * miattn_split_heuristic with this library's MI355X capacity (256 compute
+ * units, one decode workgroup each), 16-token pages as blocks, work units =
+ * batch x kv-head groups of a workgroup, at most 256 splits; the smallest
+ * candidate reaching the best efficiency is taken. */
 int miattn_decode_pick_splits(int batch, int num_kv_heads, int max_seq_len);
 
 /* The split-count rule described in "Why your local LLM feels dumber than it

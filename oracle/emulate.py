@@ -56,13 +56,15 @@ def log32(x) -> float:
 
 
 def fa2_split_count(total_tokens: int, sm_count: int, kv_heads: int = 4, batch: int = 1,
-                    block_tokens: int = 64, max_splits: int = 128, blocks_per_sm: int = 2):
+                    block_tokens: int = 64, max_splits: int = 128, blocks_per_sm: int = 2,
+                    threshold: float = 0.85):
     """The split-count rule described in "Why FlashAttention 2 selects 54, 62,
     or 87 groups": capacity = 2 work blocks per streaming multiprocessor; a
     candidate count s gives work ratio batch*kv_heads*s / capacity and
     efficiency ratio / ceil(ratio); counts that do not change the number of
     64-token blocks per split are skipped; the smallest count reaching 85% of
-    the best efficiency wins. Returns (splits, key_value_blocks, blocks_per_split)."""
+    the best efficiency wins (`threshold` generalizes the 85%). Returns
+    (splits, key_value_blocks, blocks_per_split)."""
     n_blocks = -(-total_tokens // block_tokens)
     capacity = blocks_per_sm * sm_count
     work = batch * kv_heads
@@ -74,7 +76,7 @@ def fa2_split_count(total_tokens: int, sm_count: int, kv_heads: int = 4, batch: 
         ratio = work * s / capacity
         cands.append((s, ratio / math.ceil(ratio)))
     best = max(e for _, e in cands)
-    s = next(c for c, e in cands if e >= 0.85 * best)
+    s = next(c for c, e in cands if e >= threshold * best)
     return s, n_blocks, -(-n_blocks // s)
 
 

@@ -201,12 +201,17 @@ def decode_brute(scores, values):
 #  normalized fp32 partial outputs weighted by exp(LSE_s - max LSE) described
 #  under "Backend names expand into four decode algorithms")
 # --------------------------------------------------------------------------
-def page_split_ranges(n_pages: int, num_splits: int):
-    """Contiguous, page-aligned groups with equal page counts
-    ceil(n_pages / num_splits); trailing groups may be empty."""
+def page_split_ranges(n_pages: int, num_splits: int, table_pages: int = None):
+    """Contiguous, page-aligned groups of ceil(table_pages / num_splits) pages
+    each (table_pages defaults to n_pages, the sequence's own page count);
+    groups past the sequence's end are empty. With one sequence that fills its
+    block table this is the equal-count partition of "Why the calculation is
+    split into groups"; in a batch the group size comes from the table width,
+    so every sequence is cut into groups of the same size."""
     if num_splits < 1:
         raise ValueError("num_splits must be >= 1")
-    pps = -(-n_pages // num_splits) if n_pages > 0 else 0
+    basis = n_pages if table_pages is None else table_pages
+    pps = -(-basis // num_splits) if basis > 0 else 0
     return [(min(s * pps, n_pages), min((s + 1) * pps, n_pages)) for s in range(num_splits)]
 
 
@@ -214,7 +219,8 @@ def decode_split_partials(q, k_cache, v_cache, block_table, seq_lens, scale: flo
                           num_splits: int):
     """Per (sequence, q-head, split): the normalized partial output
     O_s = sum w v / l over the split's keys and LSE_s = m_s + ln l_s, with
-    (0, -inf) for an empty split. Returns po [B*Hq, S, D], plse [B*Hq, S]."""
+    (0, -inf) for an empty split; groups are page_split_ranges with the block
+    table width as the basis. Returns po [B*Hq, S, D], plse [B*Hq, S]."""
     q = np.asarray(q, dtype=np.float64)
     B, Hq, D = q.shape
     P = k_cache.shape[1]
@@ -228,7 +234,7 @@ def decode_split_partials(q, k_cache, v_cache, block_table, seq_lens, scale: flo
             continue
         K, V = gather_sequence_kv(k_cache, v_cache, block_table, L, b)
         n_pages = (L + P - 1) // P
-        for s, (p0, p1) in enumerate(page_split_ranges(n_pages, num_splits)):
+        for s, (p0, p1) in enumerate(page_split_ranges(n_pages, num_splits, block_table.shape[1])):
             t0, t1 = p0 * P, min(p1 * P, L)
             if t1 <= t0:
                 continue

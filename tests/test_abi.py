@@ -152,10 +152,17 @@ def test_split_rule_rejects_bad_input():
 
 
 def test_pick_splits_policy():
-    for B, Hkv, ctx in [(1, 4, 16384), (1, 4, 131072), (64, 8, 4096), (1, 1, 27525)]:
+    # same candidates and efficiency as the pages' rule, MI355X capacity (256
+    # workgroups of up to 8 kv heads), smallest candidate with the best efficiency
+    for B, Hkv, ctx in [(1, 4, 16384), (1, 4, 131072), (64, 8, 4096), (1, 1, 27525), (3, 16, 9000), (7, 6, 40000)]:
         s = mi.decode_pick_splits(B, Hkv, ctx)
-        assert s == E.fa2_split_count(ctx, 256, kv_heads=Hkv, batch=B, block_tokens=16, max_splits=256)[0]
+        hw = next(h for h in (8, 4, 2, 1) if Hkv % h == 0)
+        want = E.fa2_split_count(ctx, 256, kv_heads=Hkv // hw, batch=B, block_tokens=16, max_splits=256,
+                                 blocks_per_sm=1, threshold=1.0)[0]
+        assert s == want
         assert 1 <= s <= 256
+    assert mi.decode_pick_splits(64, 8, 4096) == 4
+    assert mi.decode_pick_splits(1, 4, 131072) == 256
 
 
 def test_workspace_bytes():
