@@ -59,6 +59,17 @@ __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
+// Direct HBM -> LDS copy of 16 bytes per lane through a buffer resource
+// (MUBUF "lds" form): lane i's 16 bytes from base + voff land at
+// lds + 16 i. The buffer form, unlike the global one, is tracked by the
+// compiler as a plain vector-memory load, so LDS reads issued while it is in
+// flight keep their own fine-grained lgkmcnt waits. base must be uniform.
+__device__ __forceinline__ void dma16_to_lds(const void* base, uint32_t voff, MIATTN_LDS void* lds) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 lds_ld16(const MIATTN_LDS void* p) {
   return *reinterpret_cast<const MIATTN_LDS u32x4*>(p);
 }

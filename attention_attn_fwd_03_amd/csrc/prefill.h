@@ -13,13 +13,12 @@
 //    operand read from LDS feeds QB MFMAs (LDS bytes per flop halve at QB=2)
 //    and all waves reuse the same K/V tile (GQA sharing of "GPU Datapath",
 //    section C).
-//  * K/V tiles of Bc = 32*KB keys are double-buffered in LDS. Tiles are
-//    fetched into registers with coalesced 16-byte loads (K two tiles ahead,
-//    V one ahead) and written to LDS at the end of the iteration; one barrier
-//    per tile.
-//  * Software pipeline inside each wave: while the vector ALUs turn tile j's
-//    scores into probabilities, the matrix cores already compute tile j+1's
-//    scores, then consume tile j's probabilities in P.V.
+//  * K/V tiles of Bc = 32*KB keys are double-buffered in LDS and copied
+//    straight from HBM into LDS (buffer loads in their LDS form, 16 bytes per
+//    lane, whole rows per 16 lanes) one tile ahead, into a swizzled layout
+//    that keeps the MFMA operand reads free of bank conflicts; one barrier
+//    per tile. Two workgroups share each CU, so one's softmax overlaps the
+//    other's matrix-core work.
 //  * S^T = K . Q^T on 32x32x16 bf16 MFMAs: lane l owns query row l%32 and 16
 //    of every 32 keys (the other 16 sit in lane l^32), so row max and row sum
 //    are in-lane reductions plus one v_permlane32_swap.
@@ -168,10 +167,8 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
         ko -= back;
         vo -= back;
       }
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(kb0 + ko),
-                                       (MIATTN_LDS void*)(kbuf(buf) + (wave * TL::NI + j) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(vb0 + vo),
-                                       (MIATTN_LDS void*)(vbuf(buf) + (wave * TL::NI + j) * 1024), 16, 0, 0);
+      dma16_to_lds(kb0, ko, kbuf(buf) + (wave * TL::NI + j) * 1024);
+      dma16_to_lds(vb0, vo, vbuf(buf) + (wave * TL::NI + j) * 1024);
     }
   };
 

@@ -88,12 +88,15 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
 /*
  * miattn_attn_decode_paged -- one query token per sequence against a paged
  * KV cache ("GPU Datapath", section D: block table of 16-token pages, pages in
- * any order), evaluated split-KV: the context of each sequence is cut into
- * num_splits contiguous, page-aligned groups of ceil(pages / num_splits)
- * pages, each group yields a normalised partial output and its log-sum-exp,
- * and the groups are merged by log-sum-exp weights ("Why your local LLM feels
- * dumber than it is", sections "Why the calculation is split into groups" and
- * "Backend names expand into four decode algorithms", FlashAttention 2 entry).
+ * any order), evaluated split-KV: split s of every sequence covers logical
+ * pages [s * P, (s + 1) * P) with P = ceil(max_pages_per_seq / num_splits)
+ * (equal-size, page-aligned groups sized from the block-table width; the
+ * pages past a sequence's own length are skipped, so its last groups may be
+ * short or empty), each group yields a normalised partial output and its
+ * log-sum-exp, and the groups are merged by log-sum-exp weights ("Why your
+ * local LLM feels dumber than it is", sections "Why the calculation is split
+ * into groups" and "Backend names expand into four decode algorithms",
+ * FlashAttention 2 entry). An empty group contributes weight 0.
  *
  *   q        [batch, Hq, D]                         bf16
  *   k_cache, v_cache [num_pages, 16, Hkv, D]        bf16
@@ -103,10 +106,12 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
  *            cached for each sequence (the query sees all of them)
  *   o        [batch, Hq, D] bf16 (written); lse [batch, Hq] float32 (written;
  *            may be NULL). A sequence of length 0 gives o = 0, lse = -inf.
- *   page_size must be MIATTN_PAGE_SIZE; head_dim 64, 128 or 256; Hq/Hkv <= 16.
+ *   page_size must be MIATTN_PAGE_SIZE; head_dim 64, 128 or 256; Hq/Hkv <= 8
+ *            (MIATTN_ERR_UNSUPPORTED otherwise).
  *   num_splits: >= 1 to fix the split count, 0 to let the library choose
- *            (miattn_decode_pick_splits). Bitwise reproducibility holds for a
- *            fixed split count.
+ *            (miattn_decode_pick_splits); counts above max_pages_per_seq are
+ *            lowered to it. Bitwise reproducibility holds for a fixed split
+ *            count.
  *   workspace / workspace_bytes: device scratch for the split partials
  *            (miattn_decode_workspace_bytes bytes). workspace == NULL uses a
  *            buffer the library allocates and caches per device (grown on
