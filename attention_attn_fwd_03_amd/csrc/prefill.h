@@ -63,24 +63,25 @@ struct FwdArgs {
 constexpr float kFwdRescaleThreshold = 8.0f;
 
 // LDS tile of BC rows x D bf16, stored unpadded as 16-byte slots; chunk c of
-// row r sits in slot c ^ swz(r). K uses swz = r mod 16 (the 128-bit operand
-// reads of 16 consecutive rows hit 16 different bank groups); V uses
-// 2 (r mod 8) + bit 3 of r (the transposing reads of 4 consecutive rows x 2
-// chunks hit 8 different bank groups). Tiles are filled by direct global->LDS
-// loads of whole rows (16 lanes x 16 B per row), so global reads stay
-// row-contiguous.
+// row r sits in slot c ^ swz(r). LDS serves 256 bytes (64 banks) per cycle,
+// i.e. 16 slots; a row of D = 128 spans all 64 banks, D = 64 half of them.
+// K: a 128-bit operand read serves 16 lanes = 16 consecutive rows x one
+// chunk per cycle; swz = r mod 16 (D = 64: (r / 2) mod 8, since two rows
+// share the banks) puts them in 16 different slots. V: a transposing read
+// serves 32 lanes = 4 consecutive rows x 4 consecutive chunks (a 4-aligned
+// group) per cycle; swz = 4 (r mod 4) (D = 64: 4 ((r / 2) mod 2)) moves each
+// row's group to its own quarter of the banks. Tiles are filled by direct
+// HBM->LDS copies of whole rows (16 lanes x 16 B per row for D = 128), so
+// the HBM reads stay row-contiguous.
 template <int D, int KB>
 struct FwdTile {
   static constexpr int BC = 32 * KB;
   static constexpr int CH = D / 8;                      // 16-byte chunks per row
-  static constexpr int SWZ_MASK = (CH < 16 ? CH : 16) - 1;
   static constexpr int TILE_BYTES = BC * D * 2;
   static constexpr int NI = TILE_BYTES / 1024 / 4;      // 1-KB direct loads per wave per tile
   static_assert(TILE_BYTES % 4096 == 0, "tile must split into 1-KB loads over 4 waves");
-  __device__ static int kswz(int r) { return r & SWZ_MASK; }
-  __device__ static int vswz(int r) {
-    return CH >= 16 ? (((r & 7) << 1) | ((r >> 3) & 1)) & SWZ_MASK : (((r & 3) << 1) | ((r >> 2) & 1)) & SWZ_MASK;
-  }
+  __device__ static int kswz(int r) { return CH >= 16 ? (r & 15) : ((r >> 1) & (CH - 1)); }
+  __device__ static int vswz(int r) { return CH >= 16 ? 4 * (r & 3) : 4 * ((r >> 1) & 1); }
 };
 
 // QB = 32-row query blocks per wave (1 or 2); KB = 32-key blocks per tile.
