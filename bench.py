@@ -52,36 +52,102 @@ def traffic_from_profile(kernel_key: str, launches_bytes_alg: float):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    ent = rec.get(kernel_key)
+    ent = rec.get("kernels", {}).get(kernel_key)
     if not ent or ent.get("source_hash") != kernel_source_hash():
         return None
     return ent.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(prefill_case, heads_sample: int = 8):
+def cpu_baseline(prefill_case, min_seconds: float = 10.0, max_reps: int = 8):
     """The fp64 oracle timed on the host cores on a bounded sample of the
-    prefill workload (the first `heads_sample` query heads)."""
+    prefill workload: the whole causal GQA problem (all query heads), run
+    until at least `min_seconds` of CPU time have accumulated."""
     import oracle
     from attention_attn_fwd_03_amd import accounting
     q, k, v = prefill_case.as_f64()
-    Hkv_s = max(1, heads_sample * prefill_case.num_kv_heads // prefill_case.num_q_heads)
-    qs = np.ascontiguousarray(q[:, :heads_sample])
-    ks = np.ascontiguousarray(k[:, :Hkv_s])
-    vs = np.ascontiguousarray(v[:, :Hkv_s])
-    t0 = time.perf_counter()
-    oracle.attention_dense(qs, ks, vs, prefill_case.cu_seqlens, heads_sample, Hkv_s, prefill_case.scale, True)
-    dt = time.perf_counter() - t0
-    fl = accounting.prefill_flops(prefill_case.seqlens, heads_sample, prefill_case.head_dim, True)
+    H, Hkv = prefill_case.num_q_heads, prefill_case.num_kv_heads
+    reps, t_total = 0, 0.0
+    while reps < max_reps and (reps == 0 or t_total < min_seconds):
+        t0 = time.perf_counter()
+        oracle.attention_dense(q, k, v, prefill_case.cu_seqlens, H, Hkv, prefill_case.scale, True)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    fl = accounting.prefill_flops(prefill_case.seqlens, H, prefill_case.head_dim, True) * reps
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"causal GQA prefill S={prefill_case.total_tokens}, D={prefill_case.head_dim}, "
-                      f"{heads_sample} of {prefill_case.num_q_heads} query heads ({Hkv_s} kv heads), "
-                      f"fp64 numpy materialized form, {dt:.2f} s; host has "
-                      f"{len(os.sched_getaffinity(0))} usable cores"}
+    return {"value": fl / t_total / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the causal GQA prefill S={prefill_case.total_tokens}, Hq={H}, Hkv={Hkv}, "
+                      f"D={prefill_case.head_dim} (all heads), {reps} run(s), {t_total:.1f} s; fp64 numpy "
+                      f"materialized form; host has {len(os.sched_getaffinity(0))} usable cores"}
+
+
+# kernels whose HBM traffic the counter summary records: key -> (stage run by
+# --only, kernel-name substrings of one launch)
+TRAFFIC_KERNELS = {
+    "prefill_causal_gqa_s4096": ("prefill", ["miattn_prefill_fwd_kernel"]),
+    "decode_paged_b64": ("decode", ["miattn_decode_split_kernel", "miattn_combine_kernel"]),
+    "decode_long_ctx131072": ("long", ["miattn_decode_split_kernel", "miattn_combine_kernel"]),
+}
+
+
+def summarize_counters(root: str):
+    """Turn rocprofv3 --pmc runs into profiles/hbm_traffic.json.
+
+    `root` holds one rocprofv3 output directory per (stage, counter), named
+    `<stage>_FETCH_SIZE` / `<stage>_WRITE_SIZE`, for the stages prefill, decode,
+    long and copy (the last from --only copy, a 1 GiB device copy). Counter
+    values are KiB per dispatch; each is scaled by (true bytes / counter
+    bytes) of the copy, which reads and writes exactly 1 GiB."""
+    import csv
+    import glob
+    import sqlite3
+
+    def per_dispatch(stage, counter):
+        """median over dispatches of each kernel's counter value (rocprofv3
+        writes a rocpd SQLite database, or CSV with --output-format csv)"""
+        d = os.path.join(root, f"{stage}_{counter}")
+        vals = {}
+        for fn in glob.glob(os.path.join(d, "**", "*.db"), recursive=True):
+            con = sqlite3.connect(fn)
+            for name, disp, v in con.execute(
+                    "select kernel_name, dispatch_id, value from counters_collection where counter_name = ?",
+                    (counter,)):
+                vals[(name, disp)] = vals.get((name, disp), 0.0) + float(v)   # sum over instances
+            con.close()
+        for fn in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(fn) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") == counter:
+                        key = (r["Kernel_Name"], r.get("Dispatch_Id", ""))
+                        vals[key] = vals.get(key, 0.0) + float(r["Counter_Value"])
+        by_kernel = {}
+        for (name, _), v in vals.items():
+            by_kernel.setdefault(name, []).append(v)
+        return {n: float(np.median(v)) for n, v in by_kernel.items()}
+
+    cal = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        d = per_dispatch("copy", counter)
+        kib = max(d.values())   # the copy kernel is the dispatch with the most traffic
+        cal[counter] = (1 << 30) / (kib * 1024.0)
+    out = {"counter_unit": "KiB per dispatch", "calibration_1GiB_copy": cal,
+           "source_hash": kernel_source_hash(), "kernels": {}}
+    for key, (stage, names) in TRAFFIC_KERNELS.items():
+        rec = {}
+        for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+            d = per_dispatch(stage, counter)
+            kib = sum(v for n, v in d.items() if any(s in n for s in names))
+            rec[counter] = {"raw_kib": kib, "bytes": kib * 1024.0 * cal[counter]}
+        rec["hbm_bytes_per_launch"] = rec["FETCH_SIZE"]["bytes"] + rec["WRITE_SIZE"]["bytes"]
+        rec["source_hash"] = out["source_hash"]
+        out["kernels"][key] = rec
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    with open(path, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out), flush=True)
 
 
 def main():
@@ -95,7 +161,12 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "long", "copy"], default=None,
                     help="profiling aid: run just one stage (or a 1 GiB device copy used to calibrate "
                          "the HBM byte counters) for --steps iterations and print its mean time")
+    ap.add_argument("--summarize-counters", metavar="DIR", default=None,
+                    help="write profiles/hbm_traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
                                    "not implemented", "n_gpus": args.gpus}), flush=True)
@@ -230,7 +301,8 @@ def main():
                         "algorithmic_gflop": round(fl_pre / 1e9, 3)},
             "decode_paged": {"B": dc.batch, "tokens": int(dc.seq_lens.sum()), "splits": dsplits,
                              "ms": round(t_dec * 1e3, 4), "GB/s": round(gbs_dec, 1),
-                             "frac_hbm": round(gbs_dec / PEAK_HBM_GBS, 4), "algorithmic_MB": round(by_dec / 1e6, 2)},
+                             "frac_hbm": round(gbs_dec / PEAK_HBM_GBS, 4), "algorithmic_MB": round(by_dec / 1e6, 2),
+                             "traffic": traffic_from_profile("decode_paged_b64", by_dec)},
             "decode_long": {"ctx": 131072, "splits": lsplits, "ms": round(t_long * 1e3, 4),
                             "GB/s": round(gbs_long, 1), "frac_hbm": round(gbs_long / PEAK_HBM_GBS, 4),
                             "algorithmic_MB": round(by_long / 1e6, 2)},
@@ -238,7 +310,7 @@ def main():
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "miattn_prefill_fwd_kernel<128,2,true>",
+                     "kernel": "miattn_prefill_fwd_kernel<128,1,2,true>",
                      "per_launch_work": f"{fl_pre:.6g} FLOP"},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs_long, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(gbs_long / PEAK_HBM_GBS, 4),
