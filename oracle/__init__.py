@@ -16,6 +16,9 @@ float64, on the exact upcasts of the bits the GPU receives.
 Forms:
 - ``attention_dense`` / ``decode_dense``: materialized scores per (sequence,
   head), the naive form of "GPU Datapath", section C, harmless on a CPU.
+- ``prefill_paged_dense``: the same materialized form for a chunk of query
+  rows against a paged cache holding the whole sequence (queries aligned to
+  the end of the sequence for causal masking).
 - ``attention_brute`` / ``decode_brute``: pure-Python loops with ``math.fsum``
   for tiny inputs and the worked example.
 - ``decode_split_partials`` + ``combine_partials``: the split-into-groups form
@@ -37,6 +40,7 @@ from .reference import (  # noqa: F401
     attention_rows,
     decode_dense,
     decode_brute,
+    prefill_paged_dense,
     gather_sequence_kv,
     page_split_ranges,
     decode_split_partials,

@@ -16,6 +16,10 @@ Readings where the pages are silent:
 - causal: key j is admissible for query i when j <= i, positions counted from
   the start of each sequence (Sq = Sk per sequence).
 - decode: the one query token sees every cached token, seq_lens[b] of them.
+- chunked prefill (a query chunk of Lq tokens against a cache of Lk >= Lq
+  tokens that already holds the chunk's own keys): the chunk is the last Lq
+  positions of the sequence, so with causal masking query i sees keys
+  j <= i + (Lk - Lq) ("bottom-right" alignment); without it, all Lk keys.
 - an empty key set gives O = 0 and LSE = -inf.
 Inputs are float64 arrays (exact upcasts of bf16/fp32 storage).
 """
@@ -158,6 +162,44 @@ def gather_sequence_kv(k_cache, v_cache, block_table, seq_len: int, b: int):
     K = np.concatenate([k_cache[p] for p in pages], axis=0)[:seq_len]
     V = np.concatenate([v_cache[p] for p in pages], axis=0)[:seq_len]
     return np.asarray(K, dtype=np.float64), np.asarray(V, dtype=np.float64)
+
+
+def prefill_paged_dense(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k,
+                        num_q_heads: int, num_kv_heads: int, scale: float, causal: bool):
+    """Chunked prefill against a paged cache: sequence b has the query rows
+    q[cu_seqlens_q[b]:cu_seqlens_q[b+1]] (Lq of them) and Lk = seq_lens_k[b]
+    cached keys/values (pages through block_table[b], as in
+    gather_sequence_kv). With causal masking query i sees keys
+    j <= i + (Lk - Lq); a query that sees no key gets O = 0, LSE = -inf.
+    q [Tq, Hq, D]; returns O [Tq, Hq, D] and LSE [Hq, Tq] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    Tq, Hq, D = q.shape
+    assert Hq == num_q_heads and k_cache.shape[2] == num_kv_heads
+    group = num_q_heads // num_kv_heads
+    O = np.zeros((Tq, Hq, v_cache.shape[3]), dtype=np.float64)
+    LSE = np.full((Hq, Tq), NEG_INF, dtype=np.float64)
+    cu = [int(x) for x in cu_seqlens_q]
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        Lq, Lk = s1 - s0, int(seq_lens_k[b])
+        if Lq <= 0:
+            continue
+        K, V = gather_sequence_kv(k_cache, v_cache, block_table, Lk, b)
+        if causal:
+            i = np.arange(Lq)[:, None]
+            j = np.arange(Lk)[None, :]
+            mask = j > i + (Lk - Lq)
+        else:
+            mask = None
+        for h in range(Hq):
+            g = h // group
+            S = scale * (q[s0:s1, h, :] @ K[:, g, :].T)
+            if mask is not None:
+                S[mask] = NEG_INF
+            o, l = _softmax_rows(S, V[:, g, :])
+            O[s0:s1, h] = o
+            LSE[h, s0:s1] = l
+    return O, LSE
 
 
 def decode_dense(q, k_cache, v_cache, block_table, seq_lens, scale: float):

@@ -171,6 +171,34 @@ class DecodeCase:
         return bf16_to_f64(self.q), bf16_to_f64(self.k_cache), bf16_to_f64(self.v_cache)
 
 
+def _fill_pages(k_tok, v_tok, ctx_lens, phys, total_pages: int, tail: str):
+    """Scatter each sequence's token rows (concatenated in k_tok / v_tok) into
+    16-token physical pages in the order given by ``phys``; returns the caches
+    and the block table (-1 past each sequence's last page)."""
+    P = PAGE_SIZE
+    B = len(ctx_lens)
+    Hkv, D = k_tok.shape[1], k_tok.shape[2]
+    pages_per = [(c + P - 1) // P for c in ctx_lens]
+    max_pages = max(pages_per) if B else 0
+    fill = np.float32(np.nan) if tail == "nan" else np.float32(0.0)
+    kc = np.full((total_pages, P, Hkv, D), fill, dtype=np.float32)
+    vc = np.full((total_pages, P, Hkv, D), fill, dtype=np.float32)
+    bt = np.full((B, max(max_pages, 1)), -1, dtype=np.int32)
+    nxt = 0
+    off = 0
+    for b, c in enumerate(ctx_lens):
+        for p in range(pages_per[b]):
+            pp = int(phys[nxt])
+            nxt += 1
+            bt[b, p] = pp
+            lo = p * P
+            hi = min(c, lo + P)
+            kc[pp, : hi - lo] = k_tok[off + lo: off + hi]
+            vc[pp, : hi - lo] = v_tok[off + lo: off + hi]
+        off += c
+    return kc, vc, bt
+
+
 def make_decode(cfg: int, seed: int, ctx_lens, num_q_heads: int, num_kv_heads: int,
                 head_dim: int, scale: float, shuffle: bool = True, tail: str = "nan",
                 outlier_channels: int = 0, outlier_factor: float = 8.0,
@@ -203,27 +231,78 @@ def make_decode(cfg: int, seed: int, ctx_lens, num_q_heads: int, num_kv_heads: i
     v_tok = _normal(vrng, (T, num_kv_heads, head_dim))
     if out_ch is not None:
         k_tok[:, :, out_ch] *= np.float32(outlier_factor)
-    fill = np.float32(np.nan) if tail == "nan" else np.float32(0.0)
-    kc = np.full((total_pages, P, num_kv_heads, head_dim), fill, dtype=np.float32)
-    vc = np.full((total_pages, P, num_kv_heads, head_dim), fill, dtype=np.float32)
-    bt = np.full((B, max(max_pages, 1)), -1, dtype=np.int32)
-    nxt = 0
-    off = 0
-    for b, c in enumerate(ctx_lens):
-        for p in range(pages_per[b]):
-            pp = int(phys[nxt])
-            nxt += 1
-            bt[b, p] = pp
-            lo = p * P
-            hi = min(c, lo + P)
-            kc[pp, : hi - lo] = k_tok[off + lo: off + hi]
-            vc[pp, : hi - lo] = v_tok[off + lo: off + hi]
-        off += c
+    kc, vc, bt = _fill_pages(k_tok, v_tok, ctx_lens, phys, total_pages, tail)
     return DecodeCase(name or f"cfg{cfg}", bf16_bits(q), bf16_bits(kc), bf16_bits(vc), bt,
                       np.asarray(ctx_lens, dtype=np.int32), num_q_heads, num_kv_heads,
                       head_dim, float(np.float32(scale)), P,
                       {"outlier_channels": None if out_ch is None else out_ch.tolist(),
                        "shuffled": shuffle, "tail": tail})
+
+
+@dataclass
+class ChunkedCase:
+    """Chunked prefill: query chunks packed by cu_seqlens_q against a paged
+    cache holding every sequence's seq_lens_k tokens (the chunk's own last)."""
+    name: str
+    q: np.ndarray                # [Tq, Hq, D] bf16 bits
+    k_cache: np.ndarray          # [pages, 16, Hkv, D] bf16 bits
+    v_cache: np.ndarray
+    block_table: np.ndarray      # [n, max_pages] int32
+    cu_seqlens_q: np.ndarray     # [n + 1] int32
+    seq_lens_k: np.ndarray       # [n] int32
+    num_q_heads: int
+    num_kv_heads: int
+    head_dim: int
+    scale: float
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def q_lens(self):
+        return [int(x) for x in np.diff(self.cu_seqlens_q)]
+
+    @property
+    def total_q(self):
+        return int(self.cu_seqlens_q[-1])
+
+    @property
+    def max_seqlen_q(self):
+        return max(self.q_lens) if len(self.q_lens) else 0
+
+
+def make_chunked_prefill(cfg: int, seed: int, q_lens, k_lens, num_q_heads: int, num_kv_heads: int,
+                         head_dim: int, scale: float, shuffle: bool = True, tail: str = "nan",
+                         name: str = "") -> ChunkedCase:
+    """Query chunk b has q_lens[b] rows; sequence b caches k_lens[b] tokens in
+    16-token pages (seeded permutation with ``shuffle``). Values are drawn in
+    the order Q (all chunks), K, V (all cached tokens) from the value stream;
+    the page permutation from the structure stream. The generator does not
+    tie a chunk's queries to its cached keys: the cache is an arbitrary one."""
+    q_lens = [int(x) for x in q_lens]
+    k_lens = [int(x) for x in k_lens]
+    P = PAGE_SIZE
+    total_pages = sum((c + P - 1) // P for c in k_lens)
+    srng = np.random.default_rng([cfg, seed, 1])
+    phys = srng.permutation(total_pages) if shuffle else np.arange(total_pages)
+    vrng = np.random.default_rng([cfg, seed, 0])
+    q = _normal(vrng, (sum(q_lens), num_q_heads, head_dim))
+    k_tok = _normal(vrng, (sum(k_lens), num_kv_heads, head_dim))
+    v_tok = _normal(vrng, (sum(k_lens), num_kv_heads, head_dim))
+    kc, vc, bt = _fill_pages(k_tok, v_tok, k_lens, phys, total_pages, tail)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    return ChunkedCase(name or f"cfg{cfg}", bf16_bits(q), bf16_bits(kc), bf16_bits(vc), bt, cu,
+                       np.asarray(k_lens, dtype=np.int32), num_q_heads, num_kv_heads, head_dim,
+                       float(np.float32(scale)), {"shuffled": shuffle, "tail": tail})
+
+
+def config6(seed: int = 0, n: int = 8, chunk: int = 1024, lo: int = 0, hi: int = 6144,
+            tail: str = "nan") -> ChunkedCase:
+    """Chunked prefill: n sequences, each a chunk of `chunk` new tokens after a
+    cached prefix uniform in [lo, hi] tokens; Hq=32, Hkv=8, D=128 (the causal
+    GQA prefill shape), shuffled 16-token pages."""
+    prefix = varlen_lengths(6, seed, n, lo, hi)
+    return make_chunked_prefill(6, seed, [chunk] * n, [p + chunk for p in prefix], 32, 8, 128,
+                                1.0 / math.sqrt(128.0), shuffle=True, tail=tail,
+                                name=f"chunked_prefill_n{n}_chunk{chunk}_prefix{lo}-{hi}")
 
 
 def config3(seed: int = 0, B: int = 64, lo: int = 512, hi: int = 4096, tail: str = "nan") -> DecodeCase:
