@@ -42,6 +42,8 @@ def _load():
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.miattn_attn_fwd.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
     lib.miattn_attn_fwd.restype = I
+    lib.miattn_attn_fwd_paged.argtypes = [P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I, I, F, I, P]
+    lib.miattn_attn_fwd_paged.restype = I
     lib.miattn_attn_decode_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P, P, P]
     lib.miattn_attn_decode_paged.restype = I
     lib.miattn_attn_combine.argtypes = [P, P, I, I, I, P, P, I, P]
@@ -114,6 +116,37 @@ def attn_fwd(q, k, v, cu_seqlens, max_seqlen: int, *, scale: float, causal: bool
     _check(lib.miattn_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse) if return_lse else None,
                                _ptr(cu_seqlens), cu_seqlens.numel() - 1, int(max_seqlen), T, Hq, Hkv, D,
                                float(scale), int(bool(causal)), dt, _stream(q.device)))
+    return o, (lse if return_lse else None)
+
+
+def attn_fwd_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q: int, *,
+                   scale: float, causal: bool, out=None, lse=None, return_lse: bool = True):
+    """Chunked prefill against a paged cache. q [Tq,Hq,D] bf16 packed by
+    cu_seqlens_q (int32 [n+1]); caches [pages,16,Hkv,D] bf16; block_table
+    int32 [n,max_pages]; seq_lens_k int32 [n] (keys per sequence, the chunk's
+    own included). Returns (o [Tq,Hq,D] bf16, lse [Hq,Tq] fp32)."""
+    _need_cuda(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k, out, lse)
+    Tq, Hq, D = q.shape
+    num_pages, page, Hkv, Dk = k_cache.shape
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise ValueError("paged prefill takes bf16 q and caches")
+    if v_cache.shape != k_cache.shape or Dk != D:
+        raise ValueError("cache shapes do not match q")
+    for t, name in ((block_table, "block_table"), (cu_seqlens_q, "cu_seqlens_q"), (seq_lens_k, "seq_lens_k")):
+        if t.dtype != torch.int32:
+            raise ValueError(f"{name} must be int32")
+    n = cu_seqlens_q.numel() - 1
+    if block_table.dim() != 2 or block_table.shape[0] != n or seq_lens_k.numel() != n:
+        raise ValueError("block_table must be [n, max_pages] and seq_lens_k [n] for n sequences")
+    if not block_table.is_contiguous():
+        raise ValueError("block_table must be contiguous")
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((Hq, Tq), dtype=torch.float32, device=q.device)
+    _check(lib.miattn_attn_fwd_paged(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(o),
+                                     _ptr(lse) if return_lse else None, _ptr(cu_seqlens_q), _ptr(seq_lens_k),
+                                     _ptr(block_table), n, int(max_seqlen_q), Tq, block_table.shape[1], page,
+                                     num_pages, Hq, Hkv, D, float(scale), int(bool(causal)), _stream(q.device)))
     return o, (lse if return_lse else None)
 
 

@@ -40,3 +40,30 @@ def decode_bytes(seq_lens, num_q_heads: int, num_kv_heads: int, head_dim: int, e
 
 def decode_flops(seq_lens, num_q_heads: int, head_dim: int) -> float:
     return 4.0 * head_dim * num_q_heads * sum(int(x) for x in seq_lens)
+
+
+def chunked_prefill_flops(q_lens, k_lens, num_q_heads: int, head_dim: int, causal: bool) -> float:
+    """A chunk of Lq queries against Lk cached keys, queries aligned to the end
+    of the sequence: causal query i sees min(Lk, max(0, i + Lk - Lq + 1)) keys."""
+    pairs = 0
+    for Lq, Lk in zip(q_lens, k_lens):
+        Lq, Lk = int(Lq), int(Lk)
+        if not causal:
+            pairs += Lq * Lk
+            continue
+        off = Lk - Lq
+        for i in range(Lq):
+            pairs += min(Lk, max(0, i + off + 1))
+    return 4.0 * head_dim * num_q_heads * pairs
+
+
+def chunked_prefill_bytes(q_lens, k_lens, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                          elem_bytes: int = 2, with_lse: bool = True, page_size: int = 16) -> float:
+    """Q and O of the chunk, every cached K/V byte once, LSE, block-table entries."""
+    tq = sum(int(x) for x in q_lens)
+    tk = sum(int(x) for x in k_lens)
+    qo = 2 * tq * num_q_heads * head_dim * elem_bytes
+    kv = 2 * tk * num_kv_heads * head_dim * elem_bytes
+    lse = tq * num_q_heads * 4 if with_lse else 0
+    bt = sum((int(x) + page_size - 1) // page_size for x in k_lens) * 4
+    return float(qo + kv + lse + bt)

@@ -73,19 +73,34 @@ int check_launch(const char* what) {
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 // --- prefill launches ------------------------------------------------------
-template <int D, int QB, int KB, bool CAUSAL>
+template <int D, int QB, int KB, bool CAUSAL, bool PAGED>
 void launch_fwd(const miattn::FwdArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((miattn::miattn_prefill_fwd_kernel<D, QB, KB, CAUSAL>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((miattn::miattn_prefill_fwd_kernel<D, QB, KB, CAUSAL, PAGED>), dim3(grid), dim3(256), 0, st, a);
 }
 
-template <int D, int QB, int KB>
+template <int D, int QB, int KB, bool PAGED = false>
 void launch_fwd_c(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t st) {
-  if (causal) launch_fwd<D, QB, KB, true>(a, grid, st);
-  else launch_fwd<D, QB, KB, false>(a, grid, st);
+  if (causal) launch_fwd<D, QB, KB, true, PAGED>(a, grid, st);
+  else launch_fwd<D, QB, KB, false, PAGED>(a, grid, st);
 }
 
 // query blocks of 32 rows per wave for each head_dim
 constexpr int fwd_qb(int d) { return d >= 256 ? 1 : 1; }
+
+// bf16 prefill grid: (head slot, query-tile pair, sequence)
+long fwd_setup(miattn::FwdArgs& a, int num_seqs, int max_seqlen, int num_q_heads, int num_kv_heads, int head_dim,
+               bool unit_per_tile = false) {
+  const int G = num_q_heads / num_kv_heads;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
+  a.heads_per_wg = G >= 4 ? 4 : G;
+  const int QR = 32 * fwd_qb(head_dim) * (4 / a.heads_per_wg);
+  const int n_qtiles = (max_seqlen + QR - 1) / QR;
+  a.n_pairs = unit_per_tile ? n_qtiles : (n_qtiles + 1) / 2;
+  a.n_head_slots = num_kv_heads * (G / a.heads_per_wg);
+  return (long)a.n_head_slots * num_seqs * a.n_pairs;
+}
+
 
 template <int D>
 void launch_decode(const miattn::DecodeArgs& a, hipStream_t st) {
@@ -244,15 +259,10 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
   miattn::FwdArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
   a.o = (uint16_t*)o; a.lse = lse; a.cu_seqlens = cu_seqlens;
-  a.num_seqs = num_seqs; a.total_tokens = total_tokens;
-  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
-  a.heads_per_wg = G >= 4 ? 4 : G;
-  const int QR = 32 * fwd_qb(head_dim) * (4 / a.heads_per_wg);
-  const int n_qtiles = (max_seqlen + QR - 1) / QR;
-  a.n_pairs = (n_qtiles + 1) / 2;
-  a.n_head_slots = num_kv_heads * (G / a.heads_per_wg);
+  a.total_tokens = total_tokens;
   a.c = c;
-  const long grid = (long)a.n_head_slots * num_seqs * a.n_pairs;
+  a.seq_lens_k = nullptr; a.block_table = nullptr; a.max_pages = 0; a.num_pages = 0;
+  const long grid = fwd_setup(a, num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim);
   if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: problem too large");
   const bool cz = causal != 0;
   switch (head_dim) {
@@ -261,6 +271,52 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
     default: launch_fwd_c<256, fwd_qb(256), 1>(a, (int)grid, cz, st); break;
   }
   const int r = check_launch("prefill bf16");
+  return r ? r : ok();
+}
+
+int miattn_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, const int32_t* block_table,
+                          int num_seqs, int max_seqlen_q, int total_q, int max_pages_per_seq, int page_size,
+                          int num_pages, int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                          int causal, void* stream) {
+  if (num_seqs < 0 || max_seqlen_q < 0 || total_q < 0)
+    return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd_paged: negative size");
+  if (page_size != MIATTN_PAGE_SIZE)
+    return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd_paged: page_size must be %d", MIATTN_PAGE_SIZE);
+  if (num_seqs == 0 || total_q == 0) return ok();
+  if (!q || !k_cache || !v_cache || !o || !cu_seqlens_q || !seq_lens_k || !block_table)
+    return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd_paged: null pointer");
+  if (max_seqlen_q <= 0) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd_paged: max_seqlen_q must be > 0");
+  if (max_pages_per_seq <= 0 || num_pages <= 0)
+    return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd_paged: max_pages_per_seq and num_pages must be > 0");
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd_paged: need Hq > 0, Hkv > 0 and Hq %% Hkv == 0");
+  if (causal != 0 && causal != 1) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd_paged: causal must be 0 or 1");
+  if (!scale_ok(scale)) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd_paged: scale must be finite and > 0");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd_paged: head_dim must be 64, 128 or 256");
+  const int G = num_q_heads / num_kv_heads;
+  if (!(G == 1 || G == 2 || G % 4 == 0))
+    return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd_paged: Hq/Hkv must be 1, 2 or a multiple of 4");
+  const int dev = current_device();
+  if (dev < 0) return dev;
+  hipStream_t st = (hipStream_t)stream;
+  miattn::FwdArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k_cache; a.v = (const uint16_t*)v_cache;
+  a.o = (uint16_t*)o; a.lse = lse; a.cu_seqlens = cu_seqlens_q;
+  a.total_tokens = total_q;
+  a.c = scale * miattn::kLog2e;
+  a.seq_lens_k = seq_lens_k; a.block_table = block_table;
+  a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
+  const long grid = fwd_setup(a, num_seqs, max_seqlen_q, num_q_heads, num_kv_heads, head_dim, true);
+  if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd_paged: problem too large");
+  const bool cz = causal != 0;
+  switch (head_dim) {
+    case 64: launch_fwd_c<64, fwd_qb(64), 2, true>(a, (int)grid, cz, st); break;
+    case 128: launch_fwd_c<128, fwd_qb(128), 2, true>(a, (int)grid, cz, st); break;
+    default: launch_fwd_c<256, fwd_qb(256), 1, true>(a, (int)grid, cz, st); break;
+  }
+  const int r = check_launch("prefill paged");
   return r ? r : ok();
 }
 

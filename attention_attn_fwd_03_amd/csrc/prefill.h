@@ -44,7 +44,7 @@ namespace miattn {
 
 struct FwdArgs {
   const uint16_t* q;          // [T, Hq, D]
-  const uint16_t* k;          // [T, Hkv, D]
+  const uint16_t* k;          // [T, Hkv, D]; paged: cache [num_pages, 16, Hkv, D]
   const uint16_t* v;
   uint16_t* o;                // [T, Hq, D]
   float* lse;                 // [Hq, T] or null
@@ -55,9 +55,14 @@ struct FwdArgs {
   int num_kv_heads;
   int group;                  // G
   int heads_per_wg;           // NH
-  int n_pairs;                // query-tile pairs per sequence (ceil(ceil(max_seqlen / QR) / 2))
+  int n_pairs;                // grid units per sequence: query-tile pairs (paged: query tiles)
   int n_head_slots;           // Hkv * G / NH
   float c;                    // scale * log2(e)
+  // paged K/V (chunked prefill): key count per sequence and page table
+  const int32_t* seq_lens_k;  // [num_seqs]
+  const int32_t* block_table; // [num_seqs, max_pages]
+  int max_pages;
+  int num_pages;
 };
 
 constexpr float kFwdRescaleThreshold = 8.0f;
@@ -85,7 +90,10 @@ struct FwdTile {
 };
 
 // QB = 32-row query blocks per wave (1 or 2); KB = 32-key blocks per tile.
-template <int D, int QB, int KB, bool CAUSAL>
+// PAGED: keys/values come from a paged cache through the block table, the
+// sequence's Lk keys end with its Lq queries (chunked prefill), and causal
+// masking aligns the queries to the end: query i sees keys j <= i + Lk - Lq.
+template <int D, int QB, int KB, bool CAUSAL, bool PAGED = false>
 __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_prefill_fwd_kernel(FwdArgs a) {
   using TL = FwdTile<D, KB>;
   constexpr int BC = TL::BC;
@@ -116,11 +124,22 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
   int s1 = a.cu_seqlens[b + 1];
   s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
   s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
-  const int L = s1 - s0;
-  const int n_tiles = (L + QR - 1) / QR;
-  // causal tiles i and n-1-i together cost the same for every pair
-  if (pair > n_tiles - 1 - pair) return;   // uniform over the workgroup
-  const int n_mine = (pair == n_tiles - 1 - pair) ? 1 : 2;
+  const int Lq = s1 - s0;   // query rows of the sequence
+  int Lk = Lq;              // keys of the sequence
+  if constexpr (PAGED) {
+    Lk = a.seq_lens_k[b];
+    Lk = Lk < 0 ? 0 : (Lk > a.max_pages * 16 ? a.max_pages * 16 : Lk);
+  }
+  const int off = Lk - Lq;  // causal: query i sees keys j <= i + off
+  const int n_tiles = (Lq + QR - 1) / QR;
+  // Causal tiles i and n-1-i together cost the same for every pair, so a
+  // workgroup takes such a pair. With a cached prefix at least as long as
+  // the chunk every tile costs about the same and pairing would only double
+  // the job size, so the paged grid has one unit per tile and, for such
+  // sequences, a workgroup takes one tile (units past the pairs exit).
+  const bool paired = !PAGED || (CAUSAL && off < Lq);
+  if (paired ? (pair > n_tiles - 1 - pair) : (pair >= n_tiles)) return;   // uniform over the workgroup
+  const int n_mine = (paired && pair != n_tiles - 1 - pair) ? 2 : 1;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -135,8 +154,8 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
   const float c = a.c;
 
   const size_t kv_row = (size_t)Hkv * D;
-  const uint16_t* kbase = a.k + (size_t)s0 * kv_row + (size_t)g * D;
-  const uint16_t* vbase = a.v + (size_t)s0 * kv_row + (size_t)g * D;
+  const uint16_t* kbase = a.k + (PAGED ? 0 : (size_t)s0 * kv_row) + (size_t)g * D;
+  const uint16_t* vbase = a.v + (PAGED ? 0 : (size_t)s0 * kv_row) + (size_t)g * D;
 
   // Direct global -> LDS loads of tile kt into buffer `buf` (K and V). Each
   // wave issues NI 1-KB loads per tensor; lane i of load j fills slot
@@ -150,26 +169,61 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
     const int lidx = (wave * TL::NI + j) * 64 + lane;
     const int r = lidx / CH;
     const int slot = lidx % CH;
-    koff[j] = (uint32_t)(((size_t)r * kv_row + 8 * (slot ^ TL::kswz(r))) * 2);
-    voff[j] = (uint32_t)(((size_t)r * kv_row + 8 * (slot ^ TL::vswz(r))) * 2);
+    const size_t rowpart = PAGED ? 0 : (size_t)r * kv_row;   // paged: the row comes per copy
+    koff[j] = (uint32_t)((rowpart + 8 * (slot ^ TL::kswz(r))) * 2);
+    voff[j] = (uint32_t)((rowpart + 8 * (slot ^ TL::vswz(r))) * 2);
   }
   const uint64_t tile_bytes = (uint64_t)BC * kv_row * 2;
+  // Paged: block-table entries [bt_w0, bt_w0 + 64) of this sequence, one per
+  // lane (invalid entries read page 0: such inputs never fault, their results
+  // are unspecified). A copy instruction covers 64 / CH consecutive rows, all
+  // inside one 16-token page, so its page is uniform.
+  int bt_w0 = -(1 << 30), bt_win = 0;
+  const int32_t* bt_row = a.block_table + (PAGED ? (size_t)b * a.max_pages : 0);
   auto load_tile = [&](int kt, int buf) {
-    const bool full = (kt + 1) * BC <= L;
-    const char* kb0 = (const char*)kbase + (uint64_t)kt * tile_bytes;
-    const char* vb0 = (const char*)vbase + (uint64_t)kt * tile_bytes;
+    if constexpr (!PAGED) {
+      const bool full = (kt + 1) * BC <= Lk;
+      const char* kb0 = (const char*)kbase + (uint64_t)kt * tile_bytes;
+      const char* vb0 = (const char*)vbase + (uint64_t)kt * tile_bytes;
 #pragma unroll
-    for (int j = 0; j < TL::NI; ++j) {
-      uint32_t ko = koff[j], vo = voff[j];
-      if (!full) {
-        const int r = ((wave * TL::NI + j) * 64 + lane) / TL::CH;
-        const int rr = kt * BC + r < L ? r : L - 1 - kt * BC;
-        const uint32_t back = (uint32_t)((size_t)(r - rr) * kv_row * 2);
-        ko -= back;
-        vo -= back;
+      for (int j = 0; j < TL::NI; ++j) {
+        uint32_t ko = koff[j], vo = voff[j];
+        if (!full) {
+          const int r = ((wave * TL::NI + j) * 64 + lane) / TL::CH;
+          const int rr = kt * BC + r < Lk ? r : Lk - 1 - kt * BC;
+          const uint32_t back = (uint32_t)((size_t)(r - rr) * kv_row * 2);
+          ko -= back;
+          vo -= back;
+        }
+        dma16_to_lds(kb0, ko, kbuf(buf) + (wave * TL::NI + j) * 1024);
+        dma16_to_lds(vb0, vo, vbuf(buf) + (wave * TL::NI + j) * 1024);
       }
-      dma16_to_lds(kb0, ko, kbuf(buf) + (wave * TL::NI + j) * 1024);
-      dma16_to_lds(vb0, vo, vbuf(buf) + (wave * TL::NI + j) * 1024);
+    } else {
+      // pages of this tile: [kt BC / 16, (kt + 1) BC / 16), clamped to the last
+      const int last_page = (Lk - 1) >> 4;
+      const int p_lo = (kt * BC) >> 4 < last_page ? (kt * BC) >> 4 : last_page;
+      if (p_lo < bt_w0 || p_lo + BC / 16 > bt_w0 + 64) {
+        bt_w0 = p_lo;
+        const int i = bt_w0 + lane;
+        int e = i < a.max_pages ? bt_row[i] : 0;
+        bt_win = (e >= 0 && e < a.num_pages) ? e : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < TL::NI; ++j) {
+        const int r = ((wave * TL::NI + j) * 64 + lane) / TL::CH;   // row in the tile
+        const int r0 = ((wave * TL::NI + j) * 64) / TL::CH;         // first row of this copy
+        const int t0 = kt * BC + r0;
+        // rows past the last key repeat it (same page: a copy never spans pages)
+        const int tl = t0 < Lk ? t0 : Lk - 1;
+        const int page = __builtin_amdgcn_readlane(bt_win, (tl >> 4) - bt_w0);
+        int t = kt * BC + r;
+        t = t < Lk ? t : Lk - 1;
+        if (t0 >= Lk) t = Lk - 1;
+        const uint64_t pbase = (uint64_t)page * 16 * kv_row * 2;
+        const uint32_t rowoff = (uint32_t)((size_t)(t & 15) * kv_row * 2);
+        dma16_to_lds((const char*)kbase + pbase, rowoff + koff[j], kbuf(buf) + (wave * TL::NI + j) * 1024);
+        dma16_to_lds((const char*)vbase + pbase, rowoff + voff[j], vbuf(buf) + (wave * TL::NI + j) * 1024);
+      }
     }
   };
 
@@ -183,7 +237,7 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       const int row = q0 + 32 * qb + (lane & 31);
-      const bool ok = row < L;
+      const bool ok = row < Lq;
       const uint16_t* qp = a.q + ((size_t)(s0 + (ok ? row : 0)) * Hq + h) * D + 8 * half;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -193,10 +247,11 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
     }
 
     const int qt_end = qt * QR + QR;
-    const int kend_wg = CAUSAL ? (L < qt_end ? L : qt_end) : L;
+    auto clampk = [&](int x) { return x < 0 ? 0 : (x > Lk ? Lk : x); };
+    const int kend_wg = CAUSAL ? clampk(qt_end + off) : Lk;
     const int n_kt = (kend_wg + BC - 1) / BC;
-    const int kend_w = CAUSAL ? (L < q0 + 32 * QB ? L : q0 + 32 * QB) : L;
-    const int n_kt_w = q0 < L ? (kend_w + BC - 1) / BC : 0;   // tiles this wave computes
+    const int kend_w = CAUSAL ? clampk(q0 + 32 * QB + off) : Lk;
+    const int n_kt_w = q0 < Lq ? (kend_w + BC - 1) / BC : 0;   // tiles this wave computes
 
     float m[QB], l[QB];
     f32x16 acc[QB][NDT];
@@ -211,7 +266,7 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
     }
 
     if (tsel > 0) __syncthreads();   // previous tile's last reads before the buffers are refilled
-    load_tile(0, 0);
+    if (n_kt > 0) load_tile(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
 
@@ -242,7 +297,7 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
           }
         }
         // mask (diagonal / tail tiles only), raw row max, lazy rescale
-        const bool need_mask = (kt + 1) * BC > L || (CAUSAL && (kt + 1) * BC - 1 > q0);
+        const bool need_mask = (kt + 1) * BC > Lk || (CAUSAL && (kt + 1) * BC - 1 > q0 + off);
         if (need_mask) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
@@ -252,7 +307,7 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int key = kt * BC + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-                const bool ok = key < L && (!CAUSAL || key <= qrow);
+                const bool ok = key < Lk && (!CAUSAL || key <= qrow + off);
                 s[qb][kb][r] = ok ? s[qb][kb][r] : kNegInf;
               }
           }
@@ -331,7 +386,7 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
     for (int qb = 0; qb < QB; ++qb) {
       float lt = l[qb] + xor32(l[qb]);
       const int qrow = q0 + 32 * qb + (lane & 31);
-      if (qrow < L) {
+      if (qrow < Lq) {
         const bool empty = !(lt > 0.f);
         const float inv = empty ? 0.f : 1.f / lt;
         uint16_t* op = a.o + ((size_t)(s0 + qrow) * Hq + h) * D + 4 * half;

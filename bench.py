@@ -90,6 +90,7 @@ TRAFFIC_KERNELS = {
     "prefill_causal_gqa_s4096": ("prefill", ["miattn_prefill_fwd_kernel"]),
     "decode_paged_b64": ("decode", ["miattn_decode_split_kernel", "miattn_combine_kernel"]),
     "decode_long_ctx131072": ("long", ["miattn_decode_split_kernel", "miattn_combine_kernel"]),
+    "chunked_prefill_8x1024": ("chunked", ["miattn_prefill_fwd_kernel"]),
 }
 
 
@@ -158,7 +159,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = library policy")
     ap.add_argument("--long-splits", type=int, default=0, help="0 = library policy")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "chunked", "copy"], default=None,
                     help="profiling aid: run just one stage (or a 1 GiB device copy used to calibrate "
                          "the HBM byte counters) for --steps iterations and print its mean time")
     ap.add_argument("--summarize-counters", metavar="DIR", default=None,
@@ -202,7 +203,7 @@ def main():
         return
 
     print("[bench] generating inputs", file=sys.stderr, flush=True)
-    want = {"prefill", "decode", "long"} if args.only is None else {args.only}
+    want = {"prefill", "decode", "long", "chunked"} if args.only is None else {args.only}
     P = Dd = Ld = None
     pc = synth.config2(S=4096, seed=0)
     if "prefill" in want:
@@ -224,6 +225,17 @@ def main():
         Ld["lse"] = torch.empty((lc.batch, lc.num_q_heads), dtype=torch.float32, device=dev)
         lsplits = args.long_splits or mi.decode_pick_splits(lc.batch, lc.num_kv_heads, lc.max_pages * 16)
 
+    cc = synth.config6(seed=0, tail="zero") if "chunked" in want else None
+    if cc is not None:
+        Cd = dict(q=bf16(cc.q), kc=bf16(cc.k_cache), vc=bf16(cc.v_cache), bt=i32(cc.block_table),
+                  cu=i32(cc.cu_seqlens_q), sk=i32(cc.seq_lens_k))
+        Cd["o"] = torch.empty_like(Cd["q"])
+        Cd["lse"] = torch.empty((cc.num_q_heads, cc.total_q), dtype=torch.float32, device=dev)
+
+    def chunked():
+        mi.attn_fwd_paged(Cd["q"], Cd["kc"], Cd["vc"], Cd["bt"], Cd["cu"], Cd["sk"], cc.max_seqlen_q,
+                          scale=cc.scale, causal=True, out=Cd["o"], lse=Cd["lse"])
+
     def prefill():
         mi.attn_fwd(P["q"], P["k"], P["v"], P["cu"], pc.max_seqlen, scale=pc.scale, causal=True,
                     out=P["o"], lse=P["lse"])
@@ -238,7 +250,7 @@ def main():
 
     stages = [prefill, decode, long_decode]
     if args.only is not None:
-        f = {"prefill": prefill, "decode": decode, "long": long_decode}[args.only]
+        f = {"prefill": prefill, "decode": decode, "long": long_decode, "chunked": chunked}[args.only]
         for _ in range(args.warmup):
             f()
         torch.cuda.synchronize()
@@ -273,6 +285,21 @@ def main():
     t_pre, t_dec, t_long = (float(np.mean(per[:, i])) * 1e-3 for i in range(3))
     step_ms = float(np.mean(per.sum(axis=1)))
 
+    # chunked prefill (a row beyond the step): timed on its own after the step
+    for _ in range(args.warmup):
+        chunked()
+    ce0 = torch.cuda.Event(enable_timing=True)
+    ce1 = torch.cuda.Event(enable_timing=True)
+    ce0.record(stream)
+    for _ in range(args.steps):
+        chunked()
+    ce1.record(stream)
+    torch.cuda.synchronize()
+    t_chunk = ce0.elapsed_time(ce1) / args.steps * 1e-3
+    fl_chunk = accounting.chunked_prefill_flops(cc.q_lens, cc.seq_lens_k, cc.num_q_heads, cc.head_dim, True)
+    by_chunk = accounting.chunked_prefill_bytes(cc.q_lens, cc.seq_lens_k, cc.num_q_heads, cc.num_kv_heads,
+                                                cc.head_dim)
+
     fl_pre = accounting.prefill_flops(pc.seqlens, pc.num_q_heads, pc.head_dim, True)
     tflops = fl_pre / t_pre / 1e12
     by_dec = accounting.decode_bytes(dc.seq_lens, dc.num_q_heads, dc.num_kv_heads, dc.head_dim)
@@ -296,7 +323,8 @@ def main():
         "data": "synthetic (seeded N(0,1), rounded to bf16)",
         "config": {
             "workload": "causal GQA prefill Hq=32 Hkv=8 D=128 S=4096 + paged decode B=64 ctx U[512,4096] "
-                        "shuffled 16-token pages + long decode B=1 Hq=16 Hkv=4 D=256 ctx=131072",
+                        "shuffled 16-token pages + long decode B=1 Hq=16 Hkv=4 D=256 ctx=131072 (one step); "
+                        "chunked prefill 8 chunks x 1024 after prefixes U[0,6144] reported beside it",
             "prefill": {"S": 4096, "Hq": 32, "Hkv": 8, "D": 128, "causal": True, "ms": round(t_pre * 1e3, 4),
                         "algorithmic_gflop": round(fl_pre / 1e9, 3)},
             "decode_paged": {"B": dc.batch, "tokens": int(dc.seq_lens.sum()), "splits": dsplits,
@@ -306,6 +334,15 @@ def main():
             "decode_long": {"ctx": 131072, "splits": lsplits, "ms": round(t_long * 1e3, 4),
                             "GB/s": round(gbs_long, 1), "frac_hbm": round(gbs_long / PEAK_HBM_GBS, 4),
                             "algorithmic_MB": round(by_long / 1e6, 2)},
+            "chunked_prefill": {"chunks": len(cc.q_lens), "chunk": cc.q_lens[0],
+                                "cached_tokens": int(cc.seq_lens_k.sum()), "Hq": 32, "Hkv": 8, "D": 128,
+                                "causal": True, "ms": round(t_chunk * 1e3, 4),
+                                "TFLOP/s": round(fl_chunk / t_chunk / 1e12, 2),
+                                "frac_mfma": round(fl_chunk / t_chunk / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                "algorithmic_gflop": round(fl_chunk / 1e9, 3),
+                                "algorithmic_MB": round(by_chunk / 1e6, 2),
+                                "traffic": traffic_from_profile("chunked_prefill_8x1024", by_chunk),
+                                "timing": "its own loop of --steps calls after the step loop"},
             "wall_s": round(wall, 4),
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",

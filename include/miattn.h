@@ -86,6 +86,41 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
                     int dtype, void* stream);
 
 /*
+ * miattn_attn_fwd_paged -- chunked prefill: each sequence's new query chunk
+ * attends to that sequence's keys/values held in a paged KV cache, the same
+ * cache layout and block table the decode path reads ("GPU Datapath", section
+ * D: 16-token pages in any order, reached through a block table; the varlen
+ * entry with a block table of section "Measuring the Real Kernels, One at a
+ * Time"). The chunk is the last Lq tokens of the sequence, whose Lk cached
+ * tokens already include the chunk's own keys.
+ *
+ *   q, o     [total_q, Hq, D] bf16 (o written); packed by cu_seqlens_q
+ *   lse      [Hq, total_q] float32 (written; may be NULL)
+ *   k_cache, v_cache [num_pages, 16, Hkv, D] bf16
+ *   cu_seqlens_q [num_seqs + 1] int32, device: sequence b's queries are rows
+ *            [cu_seqlens_q[b], cu_seqlens_q[b+1]), Lq of them
+ *   seq_lens_k [num_seqs] int32, device: Lk, the cached tokens of sequence b
+ *            (normally Lk >= Lq); logical page p of sequence b is physical
+ *            page block_table[b * max_pages_per_seq + p]
+ *   causal: 0 = every query sees all Lk keys; 1 = query i (0-based within the
+ *            chunk) sees keys j <= i + Lk - Lq (queries aligned to the end of
+ *            the sequence). A query that sees no key gets O = 0, LSE = -inf.
+ *   page_size must be MIATTN_PAGE_SIZE; head_dim 64, 128 or 256; Hq/Hkv 1, 2
+ *   or a multiple of 4. Numerics as miattn_attn_fwd with bf16.
+ *   num_seqs, max_seqlen_q, total_q, max_pages_per_seq, num_pages: host
+ *   integers that size the grid and bound the indices.
+ * Robustness: Lk is clamped to [0, max_pages_per_seq * 16]; block-table
+ * entries outside [0, num_pages) read page 0. Such inputs never fault, but
+ * their results are unspecified. With Lq == Lk, an in-order table and a
+ * contiguous cache this is exactly miattn_attn_fwd.
+ */
+int miattn_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* seq_lens_k, const int32_t* block_table,
+                          int num_seqs, int max_seqlen_q, int total_q, int max_pages_per_seq, int page_size,
+                          int num_pages, int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                          int causal, void* stream);
+
+/*
  * miattn_attn_decode_paged -- one query token per sequence against a paged
  * KV cache ("GPU Datapath", section D: block table of 16-token pages, pages in
  * any order), evaluated split-KV: split s of every sequence covers logical

@@ -83,6 +83,41 @@ def test_fwd_empty_is_noop():
     assert mi.last_error() == ""
 
 
+def _fwdp(**kw):
+    a = dict(q=1, kc=1, vc=1, o=1, lse=None, cu=1, sk=1, bt=1, n=2, maxs=16, T=20, mp=4, ps=16, npg=8, Hq=4,
+             Hkv=2, D=128, scale=0.1, causal=1)
+    a.update(kw)
+    return mi.lib.miattn_attn_fwd_paged(a["q"], a["kc"], a["vc"], a["o"], a["lse"], a["cu"], a["sk"], a["bt"],
+                                        a["n"], a["maxs"], a["T"], a["mp"], a["ps"], a["npg"], a["Hq"], a["Hkv"],
+                                        a["D"], a["scale"], a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), mi.ERR_INVALID_ARG),
+    (dict(sk=None), mi.ERR_INVALID_ARG),
+    (dict(bt=None), mi.ERR_INVALID_ARG),
+    (dict(cu=None), mi.ERR_INVALID_ARG),
+    (dict(n=-1), mi.ERR_INVALID_ARG),
+    (dict(maxs=0), mi.ERR_INVALID_ARG),
+    (dict(mp=0), mi.ERR_INVALID_ARG),
+    (dict(npg=0), mi.ERR_INVALID_ARG),
+    (dict(ps=32), mi.ERR_UNSUPPORTED),
+    (dict(D=96), mi.ERR_UNSUPPORTED),
+    (dict(Hq=12, Hkv=4), mi.ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), mi.ERR_INVALID_ARG),
+    (dict(causal=3), mi.ERR_INVALID_ARG),
+    (dict(scale=0.0), mi.ERR_INVALID_ARG),
+])
+def test_fwd_paged_validation(kw, code):
+    assert _fwdp(**kw) == code
+    assert mi.last_error() != ""
+
+
+def test_fwd_paged_empty_is_noop():
+    assert _fwdp(n=0, q=None) == mi.OK
+    assert _fwdp(T=0, q=None) == mi.OK
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(q=None), mi.ERR_INVALID_ARG),
     (dict(bt=None), mi.ERR_INVALID_ARG),
@@ -187,3 +222,15 @@ def test_accounting_flops():
     assert accounting.prefill_flops([4], 1, 1, True) == 4 * 10
     assert accounting.prefill_flops([4], 1, 1, False) == 4 * 16
     assert math.isclose(accounting.prefill_flops([4096], 32, 128, True), 137.47e9, rel_tol=1e-3)
+
+
+def test_accounting_chunked_reduces_to_prefill_and_decode():
+    from attention_attn_fwd_03_amd import accounting as A
+    for causal in (True, False):
+        assert A.chunked_prefill_flops([100, 7], [100, 7], 32, 128, causal) == \
+            A.prefill_flops([100, 7], 32, 128, causal)
+    assert A.chunked_prefill_flops([1, 1], [50, 70], 32, 128, True) == A.decode_flops([50, 70], 32, 128)
+    # 3 queries after 2 cached tokens: rows see 3, 4, 5 keys
+    assert A.chunked_prefill_flops([3], [5], 1, 1, True) == 4.0 * (3 + 4 + 5)
+    # more queries than keys: the first two see nothing
+    assert A.chunked_prefill_flops([4], [2], 1, 1, True) == 4.0 * (0 + 0 + 1 + 2)
