@@ -162,3 +162,34 @@ def test_caller_workspace():
     small = torch.empty(8, dtype=torch.float32, device="cuda")
     with pytest.raises(mi.MiattnError):
         run(case, 4, workspace=small)
+
+
+@pytest.mark.parametrize("S", [2, 4, 16])
+def test_library_and_caller_workspace_agree(S):
+    case = synth.make_decode(3, 11, [1, 900, 37, 2048, 513, 64, 17, 1500], 32, 8, 128, 1 / math.sqrt(128),
+                             shuffle=True, tail="nan", name="workspace_paths")
+    dev = to_dev(case)
+    O, L = reference(case)
+    of, lf = run(case, S, dev)
+    ws = torch.empty(mi.decode_workspace_bytes(case.batch, case.num_q_heads, case.head_dim, S),
+                     dtype=torch.uint8, device=dev[0].device)
+    oc, lc = run(case, S, dev, workspace=ws)
+    assert_bf16_close(host(of), O, f"S={S}")
+    assert_lse_close(host(lf), L, f"S={S}")
+    assert bitwise_equal(of, oc) and bitwise_equal(lf, lc)
+
+
+def test_repeatable_with_other_shapes_in_between():
+    # the library workspace is regrown and reused across shapes; results of a
+    # fixed problem keep their bits
+    a = synth.make_decode(3, 12, [700, 33, 256, 1000], 32, 8, 128, 0.088, shuffle=True, tail="zero")
+    b = synth.make_decode(3, 13, [50] * 17, 16, 4, 64, 0.125, shuffle=True, tail="zero")
+    da, db = to_dev(a), to_dev(b)
+    o1, l1 = run(a, 3, da)
+    for S in (2, 40, 7):
+        ob, lb = run(b, S, db)
+        o2, l2 = run(a, 3, da)
+        assert bitwise_equal(o1, o2) and bitwise_equal(l1, l2)
+    Ob, Lb = reference(b)
+    assert_bf16_close(host(ob), Ob, "interleaved batch")
+    assert_lse_close(host(lb), Lb, "interleaved batch")
