@@ -84,6 +84,69 @@ def cpu_baseline(prefill_case, min_seconds: float = 10.0, max_reps: int = 8):
                       f"materialized form; host has {len(os.sched_getaffinity(0))} usable cores"}
 
 
+def sweep_splits(torch, mi, dev):
+    """Paged decode time for split counts 1, 2, 4, ..., 256 on synthetic caches
+    (seeded device-side normals, shuffled 16-token pages), for the two decode
+    shapes and batch 1-64, contexts 1K-64K (fixed, and uniform in [ctx/8, ctx])."""
+    import statistics
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    rng = torch.Generator().manual_seed(1)
+
+    def make(lens, Hq, Hkv, D):
+        pages = [(L + 15) // 16 for L in lens]
+        tot, mp = sum(pages), max(pages)
+        kc = torch.randn((tot, 16, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+        vc = torch.randn((tot, 16, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+        perm = torch.randperm(tot, generator=g, device=dev).to(torch.int32)
+        bt = torch.full((len(lens), mp), -1, dtype=torch.int32, device=dev)
+        o = 0
+        for b, n in enumerate(pages):
+            bt[b, :n] = perm[o:o + n]
+            o += n
+        q = torch.randn((len(lens), Hq, D), generator=g, device=dev).to(torch.bfloat16)
+        return q, kc, vc, bt, torch.tensor(lens, dtype=torch.int32, device=dev)
+
+    def time_it(args, S, scale):
+        for _ in range(3):
+            mi.attn_decode_paged(*args, scale=scale, num_splits=S)
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(20):
+                mi.attn_decode_paged(*args, scale=scale, num_splits=S)
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) / 20 * 1e3)
+        return statistics.median(ts)
+
+    for Hq, Hkv, D in ((32, 8, 128), (16, 4, 256)):
+        for B in (1, 4, 16, 64):
+            for ctx in (1024, 4096, 16384, 65536):
+                if B * ctx > 1 << 20:
+                    continue
+                for var in (False, True):
+                    if var and B == 1:
+                        continue
+                    lens = [ctx] * B if not var else [int(x) for x in torch.randint(ctx // 8, ctx + 1, (B,),
+                                                                                        generator=rng)]
+                    args = make(lens, Hq, Hkv, D)
+                    pol = mi.decode_pick_splits(B, Hkv, max(lens))
+                    cand = sorted({1, 2, 4, 8, 16, 32, 64, 128, 256, pol})
+                    res = {S: round(time_it(args, S, D ** -0.5), 1) for S in cand if S <= (max(lens) + 15) // 16}
+                    best = min(res, key=res.get)
+                    by = 4 * sum(lens) * Hkv * D
+                    print(json.dumps({"shape": {"Hq": Hq, "Hkv": Hkv, "D": D}, "B": B, "ctx": ctx,
+                                      "lengths": "uniform [ctx/8, ctx]" if var else "fixed", "policy": pol,
+                                      "us_policy": res.get(pol), "fastest": best, "us_fastest": res[best],
+                                      "GB/s_fastest": round(by / res[best] / 1e3, 1), "us_by_splits": res}),
+                          flush=True)
+                    del args
+                    torch.cuda.empty_cache()
+
+
 # kernels whose HBM traffic the counter summary records: key -> (stage run by
 # --only, kernel-name substrings of one launch)
 TRAFFIC_KERNELS = {
@@ -162,6 +225,9 @@ def main():
     ap.add_argument("--only", choices=["prefill", "decode", "long", "chunked", "copy"], default=None,
                     help="profiling aid: run just one stage (or a 1 GiB device copy used to calibrate "
                          "the HBM byte counters) for --steps iterations and print its mean time")
+    ap.add_argument("--sweep-splits", action="store_true",
+                    help="time paged decode over split counts on a grid of batch sizes and contexts and print "
+                         "the library policy's pick beside the fastest (one JSON line per cell)")
     ap.add_argument("--summarize-counters", metavar="DIR", default=None,
                     help="write profiles/hbm_traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR")
     args = ap.parse_args()
@@ -185,6 +251,10 @@ def main():
 
     def i32(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    if args.sweep_splits:
+        sweep_splits(torch, mi, dev)
+        return
 
     if args.only == "copy":
         n = 1 << 30
