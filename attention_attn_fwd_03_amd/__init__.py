@@ -7,8 +7,12 @@ built; there is no fallback path.
 
 Entry points (same names as the C ABI, without the ``miattn_`` prefix):
     attn_fwd(q, k, v, cu_seqlens, max_seqlen, *, scale, causal) -> (o, lse)
+    attn_fwd_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k,
+                   max_seqlen_q, *, scale, causal) -> (o, lse)
     attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale,
-                      num_splits=0, max_seq_len=None) -> (o, lse)
+                      num_splits=0) -> (o, lse)
+    attn_decode_paged_numerics(..., *, scale, num_splits, numerics,
+                               tile_pages, out_dtype) -> (o, lse)
     attn_combine(partial_o, partial_lse, *, out_dtype) -> (o, lse)
 """
 from __future__ import annotations
@@ -46,6 +50,11 @@ def _load():
     lib.miattn_attn_fwd_paged.restype = I
     lib.miattn_attn_decode_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P, P, P]
     lib.miattn_attn_decode_paged.restype = I
+    lib.miattn_attn_decode_paged_numerics.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, I, P, Z, P,
+                                                      I, P, P]
+    lib.miattn_attn_decode_paged_numerics.restype = I
+    lib.miattn_decode_numerics_workspace_bytes.argtypes = [I, I, I, I]
+    lib.miattn_decode_numerics_workspace_bytes.restype = Z
     lib.miattn_attn_combine.argtypes = [P, P, I, I, I, P, P, I, P]
     lib.miattn_attn_combine.restype = I
     lib.miattn_decode_workspace_bytes.argtypes = [I, I, I, I]
@@ -185,6 +194,48 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
                                         _ptr(seq_lens), B, block_table.shape[1], page, num_pages, Hq, Hkv,
                                         D, float(scale), int(num_splits), _ptr(workspace), ws_bytes,
                                         _ptr(o), _ptr(lse) if return_lse else None, _stream(q.device)))
+    return o, (lse if return_lse else None)
+
+
+# numerics of the decode split records (miattn_attn_decode_paged_numerics)
+RECORD_LSE = 0
+RECORD_NUMERATOR_F32 = 1
+RECORD_NORMALIZED_BF16 = 2
+RECORD_NUMERATOR_BF16 = 3
+NUMERICS_ROUNDED_NORMALIZER = 4
+NUMERICS_P_FP16 = 8
+
+
+def decode_numerics_workspace_bytes(batch: int, num_q_heads: int, head_dim: int, num_splits: int) -> int:
+    return int(lib.miattn_decode_numerics_workspace_bytes(batch, num_q_heads, head_dim, num_splits))
+
+
+def attn_decode_paged_numerics(q, k_cache, v_cache, block_table, seq_lens, *, scale: float, num_splits: int,
+                               numerics: int = RECORD_LSE, tile_pages: int = 0, out_dtype=torch.bfloat16,
+                               workspace=None, out=None, lse=None, return_lse: bool = True):
+    """Paged split-KV decode with selectable split records, rounding points
+    and group geometry (see miattn_attn_decode_paged_numerics). Same inputs as
+    attn_decode_paged; returns (o [B,Hq,D] of out_dtype, lse [B,Hq] fp32)."""
+    _need_cuda(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
+    B, Hq, D = q.shape
+    num_pages, page, Hkv, Dk = k_cache.shape
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise ValueError("decode takes bf16 q and caches")
+    if v_cache.shape != k_cache.shape or Dk != D:
+        raise ValueError("cache shapes do not match q")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    dt = BF16 if out_dtype == torch.bfloat16 else FP32 if out_dtype == torch.float32 else None
+    if dt is None:
+        raise ValueError("out_dtype must be bf16 or fp32")
+    o = out if out is not None else torch.empty((B, Hq, D), dtype=out_dtype, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.miattn_attn_decode_paged_numerics(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table), _ptr(seq_lens), B, block_table.shape[1], page,
+        num_pages, Hq, Hkv, D, float(scale), int(num_splits), int(numerics), int(tile_pages), _ptr(workspace),
+        ws_bytes, _ptr(o), dt, _ptr(lse) if return_lse else None, _stream(q.device)))
     return o, (lse if return_lse else None)
 
 

@@ -109,3 +109,141 @@ __global__ __launch_bounds__(256) void miattn_combine_kernel(CombineArgs a) {
 }
 
 }  // namespace miattn
+
+namespace miattn {
+
+// Merges of split statistics records (reference max m_s in log2 units,
+// normaliser l_s, and a numerator or normalised partial per column), the
+// other three merges of "Why your local LLM feels dumber than it is",
+// section "Backend names expand into four decode algorithms":
+//   mode 1: numerators and normalisers brought to M = max m_s:
+//           O = sum_s num_s 2^(m_s-M) / sum_s l_s 2^(m_s-M);
+//   mode 2: normalised partials weighted by their corrected normalisers:
+//           O = sum_s o_s l_s 2^(m_s-M) / sum_s l_s 2^(m_s-M);
+//   mode 3: an ordered running recurrence over s = 0, 1, ...: the running
+//           state (m, l, num) is rescaled to max(m, m_s) and the split added;
+//           a running state that is still empty is not rescaled (its weight
+//           is 0) and empty splits (m_s = -inf) are skipped.
+// LSE = (M + log2 sum) ln 2 in every mode; an all-empty row gives O = 0 and
+// LSE = -inf. Modes 1 and 2 reduce in the combine kernel's fixed order; mode 3
+// is sequential per column by definition.
+struct MergeStatsArgs {
+  const float* part_o;   // [rows, S, D]
+  const float* part_m;   // [rows, S]
+  const float* part_l;   // [rows, S]
+  void* o;               // [rows, D] bf16 or fp32
+  float* lse;            // [rows] or null
+  int rows;
+  int num_splits;
+  int head_dim;
+  int out_bf16;
+  int mode;
+};
+
+__device__ __forceinline__ void store_row4(const MergeStatsArgs& a, int row, int c, f32x4 v) {
+  const int D = a.head_dim;
+  if (a.out_bf16) {
+    u32x2 w2 = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    *reinterpret_cast<u32x2*>((uint16_t*)a.o + (size_t)row * D + 4 * c) = w2;
+  } else {
+    *reinterpret_cast<f32x4*>((float*)a.o + (size_t)row * D + 4 * c) = v;
+  }
+}
+
+// Grid: (rows, ceil(D / 128)); 256 threads.
+__global__ __launch_bounds__(256) void miattn_merge_stats_kernel(MergeStatsArgs a) {
+  __shared__ float red[256];
+  __shared__ f32x4 part[256];
+  const int row = blockIdx.x;
+  const int S = a.num_splits;
+  const int D = a.head_dim;
+  const int DQ = D / 4;
+  const int col0 = blockIdx.y * kCombineCols;
+  const int ncol = DQ - col0 < kCombineCols ? DQ - col0 : kCombineCols;
+  const int t = threadIdx.x;
+  const float* pm = a.part_m + (size_t)row * S;
+  const float* pl = a.part_l + (size_t)row * S;
+  const float* po = a.part_o + (size_t)row * S * D;
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+
+  if (a.mode == 3) {
+    if (t < ncol) {
+      const int c = col0 + t;
+      float rm = kNegInf, rl = 0.f;
+      f32x4 rn = z;
+      // the recurrence is sequential; its loads are not, so they are issued
+      // kCombineUnroll splits ahead
+      for (int s0 = 0; s0 < S; s0 += kCombineUnroll) {
+        float xm[kCombineUnroll], xl[kCombineUnroll];
+        f32x4 xv[kCombineUnroll];
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+          const int s = s0 + u < S ? s0 + u : S - 1;
+          xm[u] = s0 + u < S ? pm[s] : kNegInf;
+          xl[u] = pl[s];
+          xv[u] = *reinterpret_cast<const f32x4*>(po + (size_t)s * D + 4 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+          const float ms = xm[u];
+          if (ms == kNegInf) continue;
+          const float nm = fmaxf(rm, ms);
+          const float keep = (rm == kNegInf) ? 0.f : exp2_hw(rm - nm);
+          const float take = exp2_hw(ms - nm);
+          rl = rl * keep + xl[u] * take;
+          rn = rn * keep + take * xv[u];
+          rm = nm;
+        }
+      }
+      const bool empty = !(rl > 0.f);
+      store_row4(a, row, c, empty ? z : rn * (1.f / rl));
+      if (a.lse != nullptr && c == 0) a.lse[row] = empty ? kNegInf : (rm + log2_hw(rl)) * kLn2;
+    }
+    return;
+  }
+
+  float mx = kNegInf;
+  for (int s = t; s < S; s += 256) mx = fmaxf(mx, pm[s]);
+  const float M = block_reduce(mx, red, true);
+  const bool empty = (M == kNegInf);
+  float ws = 0.f;
+  if (!empty)
+    for (int s = t; s < S; s += 256) ws += (pm[s] == kNegInf) ? 0.f : pl[s] * exp2_hw(pm[s] - M);
+  const float W = block_reduce(ws, red, false);
+
+  const int NG = 256 / ncol;
+  const int c = col0 + t % ncol;
+  const int gi = t / ncol;
+  f32x4 acc = z;
+  if (!empty && gi < NG) {
+    for (int s0 = gi; s0 < S; s0 += NG * kCombineUnroll) {
+      float xm[kCombineUnroll], xl[kCombineUnroll];
+      f32x4 xv[kCombineUnroll];
+#pragma unroll
+      for (int u = 0; u < kCombineUnroll; ++u) {
+        const int s = s0 + u * NG;
+        const int sc = s < S ? s : S - 1;
+        xm[u] = s < S ? pm[sc] : kNegInf;
+        xl[u] = pl[sc];
+        xv[u] = *reinterpret_cast<const f32x4*>(po + (size_t)sc * D + 4 * c);
+      }
+#pragma unroll
+      for (int u = 0; u < kCombineUnroll; ++u) {
+        const float f = exp2_hw(xm[u] - M);
+        const float w = a.mode == 1 ? f : f * xl[u];
+        acc += (xm[u] == kNegInf) ? z : w * xv[u];
+      }
+    }
+  }
+  part[t] = acc;
+  __syncthreads();
+  if (gi == 0) {
+    f32x4 sum = part[t];
+    for (int k = 1; k < NG; ++k) sum += part[k * ncol + t];
+    const bool none = empty || !(W > 0.f);
+    store_row4(a, row, c, none ? z : sum * (1.f / W));
+    if (a.lse != nullptr && c == 0) a.lse[row] = none ? kNegInf : (M + log2_hw(W)) * kLn2;
+  }
+}
+
+}  // namespace miattn

@@ -22,6 +22,24 @@
 // Each wave keeps its own running max / sum / output; the waves of a kv head
 // are merged through LDS in a fixed order at the end.
 //
+// Numerics variants (STUDY): the same kernel can store other split records
+// and round at other points, so that the decode programs compared in "Why
+// your local LLM feels dumber than it is" (section "Backend names expand into
+// four decode algorithms") can be run on this kernel's own arithmetic:
+//   record 0: normalised fp32 partial + LSE (the default above);
+//   record 1: fp32 numerator + reference max + normaliser;
+//   record 2: normalised partial rounded to bf16 + reference max + normaliser;
+//   record 3: numerator rounded to bf16 + reference max + normaliser;
+//   rounded_l: the normaliser sums the rounded weights that enter P.V
+//              instead of the fp32 ones;
+//   RR: tiles of 2^tile_shift pages dealt to the splits round robin (tile j
+//       to split j mod S) instead of contiguous page ranges;
+//   PF16: P rounded to fp16 instead of bf16, with V converted to fp16 (exact
+//         for bf16 values inside fp16's normal range) for an fp16 P.V MFMA.
+// The reference max is the running max the weights were taken against (in
+// log2 units of the scaled score); merge kernels for records 1-3 are in
+// combine.h.
+//
 // Per page (16 tokens) a wave computes S^T = K . Q^T with 16x16x32 bf16 MFMAs
 // (rows: tokens, columns: query heads, padded to 16), so lane l holds query
 // head l%16 for tokens 4(l/16)..4(l/16)+3. Those four probabilities, rounded
@@ -41,6 +59,8 @@ struct DecodeArgs {
   const int32_t* seq_lens;      // [B]
   float* part_o;                // [B*Hq, S, D] fp32   (num_splits > 1)
   float* part_lse;              // [B*Hq, S] fp32
+  float* part_m;                // [B*Hq, S] fp32 reference max, log2 units (records 1-3)
+  float* part_l;                // [B*Hq, S] fp32 normaliser (records 1-3)
   uint16_t* o;                  // [B, Hq, D] bf16     (num_splits == 1)
   float* lse;                   // [B, Hq] fp32 or null
   int batch;
@@ -52,6 +72,9 @@ struct DecodeArgs {
   int heads_per_wg;             // HW: kv heads served by one workgroup (8, 4, 2 or 1)
   int num_splits;
   float c;                      // scale * log2(e)
+  int record;                   // STUDY: split record 0-3
+  int rounded_l;                // STUDY: normaliser sums the rounded weights
+  int tile_shift;               // RR: log2(pages per tile)
 };
 
 constexpr int kDecodeWaves = 8;
@@ -71,11 +94,35 @@ struct DecodeSmem {
                                 + 2 * kDecodeWaves * 16 * 4;      // m and l per wave and head
 };
 
+__device__ __forceinline__ float round_bf16(float x) { return bf16lo_to_f32(pack_bf16x2(x, 0.f)); }
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Two floats -> packed fp16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float f16lo_to_f32(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[0];
+}
+__device__ __forceinline__ float f16hi_to_f32(uint32_t w) {
+  return (float)__builtin_bit_cast(f16x2, w)[1];
+}
+// Eight bf16 -> eight fp16 (exact for magnitudes in fp16's normal range).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_f16x2(bf16lo_to_f32(v[i]), bf16hi_to_f32(v[i]));
+  return r;
+}
+
 // PF = pages each wave keeps in flight (register double buffering when 2).
 template <int D>
 constexpr int decode_prefetch() { return D >= 256 ? 1 : 2; }
 
-template <int D>
+template <int D, bool RR = false, bool PF16 = false, bool STUDY = false>
 __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(DecodeArgs a) {
   constexpr int NKK = D / 32;   // 16x16x32 steps over the head dim, one 16-B chunk each
   constexpr int NDT = D / 16;   // 16-wide d tiles of the output
@@ -108,12 +155,39 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
   int L = a.seq_lens[b];
   L = L < 0 ? 0 : (L > a.max_pages * kPage ? a.max_pages * kPage : L);
   const int n_pages = (L + kPage - 1) / kPage;
-  // every split of every sequence covers the same page budget, sized from the
-  // block-table width, so sequences of different lengths balance
-  const int pps = (a.max_pages + a.num_splits - 1) / a.num_splits;
-  const int p0 = split * pps < n_pages ? split * pps : n_pages;
-  const int p1 = p0 + pps < n_pages ? p0 + pps : n_pages;
-  const int np = (p1 - p0 - phase + WPH - 1) / WPH > 0 ? (p1 - p0 - phase + WPH - 1) / WPH : 0;
+  const int S = a.num_splits;
+  // The split's pages in visiting order: its k-th page is logical page
+  // logical_page(k) of the sequence, for k < np_split.
+  int np_split;
+  int p0 = 0;
+  if constexpr (!RR) {
+    // every split of every sequence covers the same page budget, sized from
+    // the block-table width, so sequences of different lengths balance
+    const int pps = (a.max_pages + S - 1) / S;
+    p0 = split * pps < n_pages ? split * pps : n_pages;
+    const int p1 = p0 + pps < n_pages ? p0 + pps : n_pages;
+    np_split = p1 - p0;
+  } else {
+    const int sh = a.tile_shift;
+    const int n_tiles = (n_pages + (1 << sh) - 1) >> sh;
+    np_split = 0;
+    if (split < n_tiles) {
+      const int full = (n_tiles - 1 - split) / S + 1;     // tiles j = split + S r, j < n_tiles
+      const int last = split + S * (full - 1);
+      const int tail = n_pages - (last << sh);
+      np_split = ((full - 1) << sh) + (tail < (1 << sh) ? tail : (1 << sh));
+    }
+  }
+  auto logical_page = [&](int k) -> int {
+    if constexpr (!RR) {
+      return p0 + k;
+    } else {
+      const int sh = a.tile_shift;
+      return ((split + S * (k >> sh)) << sh) + (k & ((1 << sh) - 1));
+    }
+  };
+  // this wave's i-th page is the split's page phase + WPH i
+  const int np = (np_split - phase + WPH - 1) / WPH > 0 ? (np_split - phase + WPH - 1) / WPH : 0;
 
   // Q^T operand: head hl, d = 32*kk + 8*quad .. +7 (zero for padding heads).
   u32x4 qop[NKK];
@@ -129,7 +203,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
 
   const size_t row_stride = (size_t)Hkv * D;               // elements between tokens
   const size_t page_stride = (size_t)kPage * row_stride;   // elements between pages
-  const int32_t* bt = a.block_table + (size_t)b * a.max_pages + p0 + phase;
+  const int32_t* bt_row = a.block_table + (size_t)b * a.max_pages;
 
   // Block-table entries of the wave's pages, 64 at a time: lane j holds page
   // j of the current window (-1 if out of range or invalid).
@@ -138,7 +212,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
     const int i = first + lane;
     int pp = -1;
     if (i < np) {
-      pp = bt[WPH * i];
+      pp = bt_row[logical_page(phase + WPH * i)];
       pp = (pp >= 0 && pp < a.num_pages) ? pp : -1;
     }
     bt_win = pp;
@@ -177,17 +251,18 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
       s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[kk]), as_bf16x8(qop[kk]), s, 0, 0, 0);
-    const int lp = p0 + phase + WPH * i;
+    const int lp = logical_page(phase + WPH * i);
     const bool row_ok = page_ok && lp * kPage + tok < L;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      lds_st16(vstage + tok * Smem::kRowElems + 32 * kk + 8 * quad, row_ok ? vb[kk] : z);
+      lds_st16(vstage + tok * Smem::kRowElems + 32 * kk + 8 * quad,
+               row_ok ? (PF16 ? bf16x8_to_f16x8(vb[kk]) : vb[kk]) : z);
     return s;
   };
   // Online softmax for page i and O^T += V^T P^T from the staged V.
   auto accumulate = [&](int i, f32x4 s, bool page_ok) {
-    const int lp = p0 + phase + WPH * i;
+    const int lp = logical_page(phase + WPH * i);
     float t[4];
     float pm = kNegInf;
 #pragma unroll
@@ -210,14 +285,26 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = exp2_hw(t[r] - mu);
-    l += (p[0] + p[1]) + (p[2] + p[3]);
-    u32x2 pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-    const bf16x4 pop = as_bf16x4(pw);
+    const u32x2 pw = PF16 ? (u32x2){pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3])}
+                          : (u32x2){pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+    if (STUDY && a.rounded_l) {
+      // the normaliser sums the same rounded weights that enter P.V
+      if constexpr (PF16)
+        l += (f16lo_to_f32(pw[0]) + f16hi_to_f32(pw[0])) + (f16lo_to_f32(pw[1]) + f16hi_to_f32(pw[1]));
+      else
+        l += (bf16lo_to_f32(pw[0]) + bf16hi_to_f32(pw[0])) + (bf16lo_to_f32(pw[1]) + bf16hi_to_f32(pw[1]));
+    } else {
+      l += (p[0] + p[1]) + (p[2] + p[3]);
+    }
     const MIATTN_LDS uint16_t* vt = vstage + (4 * quad + (tok >> 2)) * Smem::kRowElems + 4 * (tok & 3);
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      const bf16x4 vop = as_bf16x4(lds_ld_tr16(vt + 16 * dt));
-      acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vop, pop, acc[dt], 0, 0, 0);
+      const u32x2 vw = lds_ld_tr16(vt + 16 * dt);
+      if constexpr (PF16)
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, vw), __builtin_bit_cast(f16x4, pw),
+                                                        acc[dt], 0, 0, 0);
+      else
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as_bf16x4(vw), as_bf16x4(pw), acc[dt], 0, 0, 0);
     }
   };
 
@@ -268,7 +355,6 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
 
   // merge the WPH waves of each kv head in wave order; one output row per
   // (kv head, query head in its group)
-  const int S = a.num_splits;
   for (int idx = threadIdx.x; idx < HW * G * (D / 4); idx += kDecodeThreads) {
     const int gh = idx / (G * (D / 4));           // kv head within the workgroup
     const int h = (idx / (D / 4)) % G;
@@ -286,10 +372,25 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
     }
     const bool empty = !(Lsum > 0.f);
     const float inv = empty ? 0.f : 1.f / Lsum;
+    const size_t row = (size_t)b * a.num_q_heads + (size_t)(hg * HW + gh) * G + h;
+    if (STUDY && a.record != 0) {
+      // split statistics: numerator (or normalised partial), reference max,
+      // normaliser; an empty split stores (0, -inf, 0)
+      f32x4 rec = a.record == 2 ? o * inv : o;
+      if (a.record >= 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) rec[e] = round_bf16(rec[e]);
+      }
+      *reinterpret_cast<f32x4*>(a.part_o + (row * S + split) * D + d4) = rec;
+      if (d4 == 0) {
+        a.part_m[row * S + split] = empty ? kNegInf : M;
+        a.part_l[row * S + split] = empty ? 0.f : Lsum;
+      }
+      continue;
+    }
     o *= inv;
     const float lse = empty ? kNegInf : (M + log2_hw(Lsum)) * kLn2;
-    const size_t row = (size_t)b * a.num_q_heads + (size_t)(hg * HW + gh) * G + h;
-    if (S == 1) {
+    if (!STUDY && S == 1) {
       u32x2 w2 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
       *reinterpret_cast<u32x2*>(a.o + row * D + d4) = w2;
       if (a.lse != nullptr && d4 == 0) a.lse[row] = lse;

@@ -102,10 +102,67 @@ long fwd_setup(miattn::FwdArgs& a, int num_seqs, int max_seqlen, int num_q_heads
 }
 
 
-template <int D>
+template <int D, bool RR = false, bool PF16 = false, bool STUDY = false>
 void launch_decode(const miattn::DecodeArgs& a, hipStream_t st) {
   const unsigned grid = (unsigned)((long)a.num_splits * (a.num_kv_heads / a.heads_per_wg) * a.batch);
-  hipLaunchKernelGGL((miattn::miattn_decode_split_kernel<D>), dim3(grid), dim3(miattn::kDecodeThreads), 0, st, a);
+  hipLaunchKernelGGL((miattn::miattn_decode_split_kernel<D, RR, PF16, STUDY>), dim3(grid),
+                     dim3(miattn::kDecodeThreads), 0, st, a);
+}
+
+template <int D>
+void launch_decode_study(const miattn::DecodeArgs& a, bool rr, bool pf16, hipStream_t st) {
+  if (rr) {
+    if (pf16) launch_decode<D, true, true, true>(a, st);
+    else launch_decode<D, true, false, true>(a, st);
+  } else {
+    if (pf16) launch_decode<D, false, true, true>(a, st);
+    else launch_decode<D, false, false, true>(a, st);
+  }
+}
+
+// The device's library-owned workspace, grown to at least `need` bytes.
+int library_workspace(int dev, size_t need, void** ws, const char* who) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_ws_bytes[dev] < need) {
+    if (g_ws[dev] != nullptr) {
+      // an enqueued kernel may still read the old buffer
+      if (hipDeviceSynchronize() != hipSuccess || hipFree(g_ws[dev]) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(MIATTN_ERR_HIP, "%s: releasing the workspace failed", who);
+      }
+      g_ws[dev] = nullptr;
+      g_ws_bytes[dev] = 0;
+    }
+    if (hipMalloc(&g_ws[dev], need) != hipSuccess) {
+      (void)hipGetLastError();
+      g_ws[dev] = nullptr;
+      return fail(MIATTN_ERR_HIP, "%s: workspace allocation of %zu bytes failed", who, need);
+    }
+    g_ws_bytes[dev] = need;
+  }
+  *ws = g_ws[dev];
+  return MIATTN_OK;
+}
+
+// Checks shared by the decode entry points.
+int decode_common_checks(const char* who, const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* block_table, const int32_t* seq_lens, const void* o,
+                         int max_pages_per_seq, int page_size, int num_pages, int num_q_heads, int num_kv_heads,
+                         int head_dim, float scale) {
+  if (page_size != MIATTN_PAGE_SIZE)
+    return fail(MIATTN_ERR_UNSUPPORTED, "%s: page_size must be %d", who, MIATTN_PAGE_SIZE);
+  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
+    return fail(MIATTN_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (max_pages_per_seq <= 0 || num_pages <= 0)
+    return fail(MIATTN_ERR_INVALID_ARG, "%s: max_pages_per_seq and num_pages must be > 0", who);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(MIATTN_ERR_INVALID_ARG, "%s: need Hq > 0, Hkv > 0 and Hq %% Hkv == 0", who);
+  if (num_q_heads / num_kv_heads > miattn::kDecodeMaxGroup)
+    return fail(MIATTN_ERR_UNSUPPORTED, "%s: Hq/Hkv must be <= %d", who, miattn::kDecodeMaxGroup);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(MIATTN_ERR_UNSUPPORTED, "%s: head_dim must be 64, 128 or 256", who);
+  if (!scale_ok(scale)) return fail(MIATTN_ERR_INVALID_ARG, "%s: scale must be finite and > 0", who);
+  return MIATTN_OK;
 }
 
 // kv heads per decode workgroup: the largest of 8, 4, 2, 1 dividing Hkv
@@ -351,17 +408,12 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
   if (page_size != MIATTN_PAGE_SIZE)
     return fail(MIATTN_ERR_UNSUPPORTED, "attn_decode_paged: page_size must be %d", MIATTN_PAGE_SIZE);
   if (batch == 0) return ok();
-  if (!q || !k_cache || !v_cache || !block_table || !seq_lens || !o)
-    return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: null pointer");
-  if (max_pages_per_seq <= 0 || num_pages <= 0)
-    return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: max_pages_per_seq and num_pages must be > 0");
-  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
-    return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: need Hq > 0, Hkv > 0 and Hq %% Hkv == 0");
-  if (num_q_heads / num_kv_heads > miattn::kDecodeMaxGroup)
-    return fail(MIATTN_ERR_UNSUPPORTED, "attn_decode_paged: Hq/Hkv must be <= %d", miattn::kDecodeMaxGroup);
-  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
-    return fail(MIATTN_ERR_UNSUPPORTED, "attn_decode_paged: head_dim must be 64, 128 or 256");
-  if (!scale_ok(scale)) return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: scale must be finite and > 0");
+  {
+    const int r = decode_common_checks("attn_decode_paged", q, k_cache, v_cache, block_table, seq_lens, o,
+                                       max_pages_per_seq, page_size, num_pages, num_q_heads, num_kv_heads,
+                                       head_dim, scale);
+    if (r) return r;
+  }
   int S = num_splits;
   if (S == 0) S = miattn_decode_pick_splits(batch, num_kv_heads, max_pages_per_seq * MIATTN_PAGE_SIZE);
   if (S > max_pages_per_seq) S = max_pages_per_seq;   // more splits than pages would only add empty groups
@@ -377,27 +429,10 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
   hipStream_t st = (hipStream_t)stream;
   void* ws = workspace;
   if (need > 0 && ws == nullptr) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    if (g_ws_bytes[dev] < need) {
-      if (g_ws[dev] != nullptr) {
-        // an enqueued kernel may still read the old buffer
-        if (hipDeviceSynchronize() != hipSuccess || hipFree(g_ws[dev]) != hipSuccess) {
-          (void)hipGetLastError();
-          return fail(MIATTN_ERR_HIP, "attn_decode_paged: releasing the workspace failed");
-        }
-        g_ws[dev] = nullptr;
-        g_ws_bytes[dev] = 0;
-      }
-      if (hipMalloc(&g_ws[dev], need) != hipSuccess) {
-        (void)hipGetLastError();
-        g_ws[dev] = nullptr;
-        return fail(MIATTN_ERR_HIP, "attn_decode_paged: workspace allocation of %zu bytes failed", need);
-      }
-      g_ws_bytes[dev] = need;
-    }
-    ws = g_ws[dev];
+    const int r = library_workspace(dev, need, &ws, "attn_decode_paged");
+    if (r) return r;
   }
-  miattn::DecodeArgs a;
+  miattn::DecodeArgs a{};
   a.q = (const uint16_t*)q; a.k_cache = (const uint16_t*)k_cache; a.v_cache = (const uint16_t*)v_cache;
   a.block_table = block_table; a.seq_lens = seq_lens; a.batch = batch;
   const size_t rows = (size_t)batch * num_q_heads;
@@ -425,6 +460,97 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
     if (r) return r;
   }
   return ok();
+}
+
+size_t miattn_decode_numerics_workspace_bytes(int batch, int num_q_heads, int head_dim, int num_splits) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 0) return 0;
+  const size_t rows = (size_t)batch * num_q_heads;
+  const size_t bytes = rows * (size_t)num_splits * ((size_t)head_dim + 2) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int miattn_attn_decode_paged_numerics(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* seq_lens, int batch,
+                                      int max_pages_per_seq, int page_size, int num_pages, int num_q_heads,
+                                      int num_kv_heads, int head_dim, float scale, int num_splits, int numerics,
+                                      int tile_pages, void* workspace, size_t workspace_bytes, void* o,
+                                      int out_dtype, float* lse, void* stream) {
+  const char* who = "attn_decode_paged_numerics";
+  if (batch < 0) return fail(MIATTN_ERR_INVALID_ARG, "%s: batch < 0", who);
+  if (num_splits < 0) return fail(MIATTN_ERR_INVALID_ARG, "%s: num_splits < 0", who);
+  if (numerics & ~0xF) return fail(MIATTN_ERR_UNSUPPORTED, "%s: unknown numerics bits 0x%x", who, numerics);
+  if (tile_pages < 0 || tile_pages > 1024 || (tile_pages & (tile_pages - 1)) != 0)
+    return fail(MIATTN_ERR_UNSUPPORTED, "%s: tile_pages must be 0 or a power of two <= 1024", who);
+  if (out_dtype != MIATTN_BF16 && out_dtype != MIATTN_FP32)
+    return fail(MIATTN_ERR_UNSUPPORTED, "%s: unknown out_dtype %d", who, out_dtype);
+  if (page_size != MIATTN_PAGE_SIZE)
+    return fail(MIATTN_ERR_UNSUPPORTED, "%s: page_size must be %d", who, MIATTN_PAGE_SIZE);
+  if (batch == 0) return ok();
+  {
+    const int r = decode_common_checks(who, q, k_cache, v_cache, block_table, seq_lens, o, max_pages_per_seq,
+                                       page_size, num_pages, num_q_heads, num_kv_heads, head_dim, scale);
+    if (r) return r;
+  }
+  const int record = numerics & 3;
+  const bool rr = tile_pages > 0;
+  int S = num_splits;
+  if (S == 0) S = miattn_decode_pick_splits(batch, num_kv_heads, max_pages_per_seq * MIATTN_PAGE_SIZE);
+  // more splits than pages (or tiles) would only add empty groups
+  const int units = rr ? (max_pages_per_seq + tile_pages - 1) / tile_pages : max_pages_per_seq;
+  if (S > units) S = units;
+  if (S < 1) S = 1;
+  if ((long)S * num_kv_heads * batch > 0x7fffffffL)
+    return fail(MIATTN_ERR_INVALID_ARG, "%s: splits * Hkv * batch too large", who);
+  const size_t need = miattn_decode_numerics_workspace_bytes(batch, num_q_heads, head_dim, S);
+  if (workspace != nullptr && workspace_bytes < need)
+    return fail(MIATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", who, workspace_bytes, need);
+  const int dev = current_device();
+  if (dev < 0) return dev;
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (ws == nullptr) {
+    const int r = library_workspace(dev, need, &ws, who);
+    if (r) return r;
+  }
+  const size_t rows = (size_t)batch * num_q_heads;
+  miattn::DecodeArgs a{};
+  a.q = (const uint16_t*)q; a.k_cache = (const uint16_t*)k_cache; a.v_cache = (const uint16_t*)v_cache;
+  a.block_table = block_table; a.seq_lens = seq_lens; a.batch = batch;
+  a.part_o = (float*)ws;
+  a.part_m = a.part_o + rows * (size_t)S * head_dim;
+  a.part_l = a.part_m + rows * (size_t)S;
+  a.part_lse = a.part_m;
+  a.o = nullptr; a.lse = nullptr;
+  a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
+  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = num_q_heads / num_kv_heads;
+  a.heads_per_wg = decode_heads_per_wg(num_kv_heads);
+  a.num_splits = S; a.c = scale * miattn::kLog2e;
+  a.record = record;
+  a.rounded_l = (numerics & MIATTN_NUMERICS_ROUNDED_NORMALIZER) ? 1 : 0;
+  a.tile_shift = rr ? __builtin_ctz((unsigned)tile_pages) : 0;
+  const bool pf16 = (numerics & MIATTN_NUMERICS_P_FP16) != 0;
+  switch (head_dim) {
+    case 64: launch_decode_study<64>(a, rr, pf16, st); break;
+    case 128: launch_decode_study<128>(a, rr, pf16, st); break;
+    default: launch_decode_study<256>(a, rr, pf16, st); break;
+  }
+  int r = check_launch("decode split (numerics)");
+  if (r) return r;
+  const unsigned chunks = (unsigned)((head_dim / 4 + miattn::kCombineCols - 1) / miattn::kCombineCols);
+  if (record == 0) {
+    miattn::CombineArgs c;
+    c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
+    c.rows = (int)rows; c.num_splits = S; c.head_dim = head_dim; c.out_bf16 = out_dtype == MIATTN_BF16;
+    hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3((unsigned)rows, chunks), dim3(256), 0, st, c);
+  } else {
+    miattn::MergeStatsArgs m;
+    m.part_o = a.part_o; m.part_m = a.part_m; m.part_l = a.part_l; m.o = o; m.lse = lse;
+    m.rows = (int)rows; m.num_splits = S; m.head_dim = head_dim; m.out_bf16 = out_dtype == MIATTN_BF16;
+    m.mode = record;
+    hipLaunchKernelGGL(miattn::miattn_merge_stats_kernel, dim3((unsigned)rows, chunks), dim3(256), 0, st, m);
+  }
+  r = check_launch("merge (numerics)");
+  return r ? r : ok();
 }
 
 }  // extern "C"

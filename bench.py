@@ -147,6 +147,57 @@ def sweep_splits(torch, mi, dev):
                     torch.cuda.empty_cache()
 
 
+def numerics_timing(torch, mi, dev, bf16, i32, steps: int, warmup: int):
+    """Time the decode's numerics variants (split records, rounding points,
+    round-robin tiles) beside the fast path on the paged-decode and
+    long-context workloads; one JSON line per variant."""
+    import synth
+    from attention_attn_fwd_03_amd import accounting
+
+    R = mi
+    for case in (synth.config3(seed=0, tail="zero"), synth.config4(ctx=131072, seed=0),
+                 synth.config4(ctx=32768, seed=0)):
+        args = (bf16(case.q), bf16(case.k_cache), bf16(case.v_cache), i32(case.block_table), i32(case.seq_lens))
+        pol = mi.decode_pick_splits(case.batch, case.num_kv_heads, case.max_pages * 16)
+        n_tiles8 = -(-case.max_pages // 8)
+        variants = [("fast path (attn_decode_paged)", None, pol, 0),
+                    ("LSE record", R.RECORD_LSE, pol, 0),
+                    ("fp32 numerators", R.RECORD_NUMERATOR_F32, pol, 0),
+                    ("bf16 normalised + rounded l, 16-page tiles round robin",
+                     R.RECORD_NORMALIZED_BF16 | R.NUMERICS_ROUNDED_NORMALIZER, pol, 16),
+                    ("bf16 numerators, ordered merge, one group per 8 pages", R.RECORD_NUMERATOR_BF16,
+                     n_tiles8, 8),
+                    ("LSE record, fp16 P", R.RECORD_LSE | R.NUMERICS_P_FP16, pol, 0)]
+        by = accounting.decode_bytes(case.seq_lens, case.num_q_heads, case.num_kv_heads, case.head_dim)
+        base = None
+        for label, numerics, S, tp in variants:
+            if numerics is None:
+                def f():
+                    mi.attn_decode_paged(*args, scale=case.scale, num_splits=S)
+            else:
+                def f():
+                    mi.attn_decode_paged_numerics(*args, scale=case.scale, num_splits=S, numerics=numerics,
+                                                  tile_pages=tp)
+            for _ in range(warmup):
+                f()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                f()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / steps * 1e3
+            base = base or us
+            print(json.dumps({"numerics": label, "workload": case.name, "splits": S, "tile_pages": tp,
+                              "us": round(us, 2), "GB/s": round(by / us / 1e3, 1),
+                              "frac_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4),
+                              "time_vs_fast_path": round(us / base, 3)}), flush=True)
+        del args
+        torch.cuda.empty_cache()
+
+
 # kernels whose HBM traffic the counter summary records: key -> (stage run by
 # --only, kernel-name substrings of one launch)
 TRAFFIC_KERNELS = {
@@ -228,6 +279,8 @@ def main():
     ap.add_argument("--sweep-splits", action="store_true",
                     help="time paged decode over split counts on a grid of batch sizes and contexts and print "
                          "the library policy's pick beside the fastest (one JSON line per cell)")
+    ap.add_argument("--numerics", action="store_true",
+                    help="time the decode numerics variants beside the fast path (one JSON line each)")
     ap.add_argument("--summarize-counters", metavar="DIR", default=None,
                     help="write profiles/hbm_traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR")
     args = ap.parse_args()
@@ -254,6 +307,10 @@ def main():
 
     if args.sweep_splits:
         sweep_splits(torch, mi, dev)
+        return
+
+    if args.numerics:
+        numerics_timing(torch, mi, dev, bf16, i32, args.steps, args.warmup)
         return
 
     if args.only == "copy":
@@ -422,7 +479,7 @@ def main():
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs_long, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(gbs_long / PEAK_HBM_GBS, 4),
                             "traffic": traffic_from_profile("decode_long_ctx131072", by_long),
-                            "kernel": "miattn_decode_split_kernel<256> + miattn_combine_kernel",
+                            "kernel": "miattn_decode_split_kernel<256, false, false, false> + miattn_combine_kernel",
                             "per_launch_work": f"{by_long:.6g} B"},
         "kernel_source_hash": kernel_source_hash(),
     }

@@ -185,6 +185,65 @@ int miattn_attn_combine(const float* partial_o, const float* partial_lse, int ro
  * (0 when num_splits <= 1). */
 size_t miattn_decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int num_splits);
 
+/*
+ * miattn_attn_decode_paged_numerics -- the same paged split-KV decode with the
+ * split records, rounding points and group geometry selectable, so that the
+ * decode programs compared in "Why your local LLM feels dumber than it is"
+ * (section "Backend names expand into four decode algorithms"; rounding points
+ * of "Why the calculation is split into groups") can be run with this
+ * library's arithmetic and set against each other and the exact result. It is
+ * a numerics-study entry point: miattn_attn_decode_paged is the fast path.
+ *
+ * numerics = one record kind | optional flags:
+ *   MIATTN_RECORD_LSE: each group stores its normalised fp32 partial and
+ *       fp32 LSE; log-sum-exp merge (what miattn_attn_decode_paged does).
+ *   MIATTN_RECORD_NUMERATOR_F32: fp32 numerator, reference max m_s and
+ *       normaliser l_s; merge O = sum num_s e^(m_s-M) / sum l_s e^(m_s-M).
+ *   MIATTN_RECORD_NORMALIZED_BF16: the normalised partial rounded to bf16,
+ *       m_s, l_s; merge O = sum o_s l_s e^(m_s-M) / sum l_s e^(m_s-M).
+ *   MIATTN_RECORD_NUMERATOR_BF16: the numerator rounded to bf16, m_s, l_s;
+ *       an ordered running merge over s = 0, 1, ... in which a still-empty
+ *       running state gets weight 0 and empty groups are skipped.
+ *   MIATTN_NUMERICS_ROUNDED_NORMALIZER: l_s sums the rounded weights that
+ *       enter P.V (bf16, or fp16 with the next flag) instead of fp32 ones.
+ *   MIATTN_NUMERICS_P_FP16: P is rounded to fp16 instead of bf16 and V is
+ *       converted to fp16 for the P.V product; values of V outside fp16's
+ *       range (|v| > 65504) overflow, below 2^-14 they lose precision.
+ * m_s is the running max the group's weights were taken against (it may lag
+ * the group's true max by up to 2^8 in weight), which leaves every merge exact
+ * in real arithmetic.
+ * tile_pages: 0 = contiguous groups exactly as miattn_attn_decode_paged;
+ *   a power of two <= 1024 = tiles of tile_pages pages dealt round robin,
+ *   tile j of a sequence to group j mod num_splits (counts above the number
+ *   of tiles of the table width are lowered to it).
+ * num_splits: as for miattn_attn_decode_paged (0 = library policy); the
+ *   records and the merge are used at every count, 1 included.
+ * o [batch, Hq, D] of out_dtype (MIATTN_BF16 or MIATTN_FP32, the latter for
+ *   the output before its final rounding); lse [batch, Hq] float32 or NULL.
+ * workspace: miattn_decode_numerics_workspace_bytes bytes, or NULL for the
+ *   library-owned buffer (shared with miattn_attn_decode_paged).
+ * Other arguments, layouts, limits and errors as for
+ * miattn_attn_decode_paged; unknown numerics bits or a bad tile_pages give
+ * MIATTN_ERR_UNSUPPORTED.
+ */
+#define MIATTN_RECORD_LSE                   0
+#define MIATTN_RECORD_NUMERATOR_F32         1
+#define MIATTN_RECORD_NORMALIZED_BF16       2
+#define MIATTN_RECORD_NUMERATOR_BF16        3
+#define MIATTN_NUMERICS_ROUNDED_NORMALIZER  4
+#define MIATTN_NUMERICS_P_FP16              8
+int miattn_attn_decode_paged_numerics(const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* block_table, const int32_t* seq_lens,
+                                      int batch, int max_pages_per_seq, int page_size, int num_pages,
+                                      int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                                      int num_splits, int numerics, int tile_pages, void* workspace,
+                                      size_t workspace_bytes, void* o, int out_dtype, float* lse,
+                                      void* stream);
+
+/* Bytes of workspace miattn_attn_decode_paged_numerics needs:
+ * batch * Hq * num_splits * (head_dim + 2) floats, rounded up to 256. */
+size_t miattn_decode_numerics_workspace_bytes(int batch, int num_q_heads, int head_dim, int num_splits);
+
 /* Split count chosen for num_splits == 0: the candidate set and efficiency of
  * miattn_split_heuristic with this library's MI355X capacity (256 compute
  * units, one decode workgroup each), 16-token pages as blocks, work units =

@@ -47,13 +47,13 @@ def assert_bf16_rounding_of(got, want, slop=2e-5, what=""):
     assert not bad.any(), what
 
 
-def assert_lse_close(got, want, what=""):
+def assert_lse_close(got, want, what="", tol=LSE_MAX_ABS):
     fin = np.isfinite(want)
     assert np.array_equal(np.isfinite(got), fin), what
     assert np.array_equal(got[~fin], want[~fin]), what
     mx, _ = errors(got[fin], want[fin])
     print(f"  {what} lse: max-abs {mx:.3e}", flush=True)
-    assert mx <= LSE_MAX_ABS, (what, mx)
+    assert mx <= tol, (what, mx, tol)
 
 
 def bitwise_equal(a, b):

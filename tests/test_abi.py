@@ -234,3 +234,45 @@ def test_accounting_chunked_reduces_to_prefill_and_decode():
     assert A.chunked_prefill_flops([3], [5], 1, 1, True) == 4.0 * (3 + 4 + 5)
     # more queries than keys: the first two see nothing
     assert A.chunked_prefill_flops([4], [2], 1, 1, True) == 4.0 * (0 + 0 + 1 + 2)
+
+
+def _decn(**kw):
+    a = dict(q=1, kc=1, vc=1, bt=1, sl=1, B=2, mp=4, ps=16, npg=8, Hq=4, Hkv=2, D=128, scale=0.1, S=2, num=0,
+             tp=0, ws=None, wsb=0, o=1, odt=0, lse=None)
+    a.update(kw)
+    return mi.lib.miattn_attn_decode_paged_numerics(a["q"], a["kc"], a["vc"], a["bt"], a["sl"], a["B"], a["mp"],
+                                                    a["ps"], a["npg"], a["Hq"], a["Hkv"], a["D"], a["scale"],
+                                                    a["S"], a["num"], a["tp"], a["ws"], a["wsb"], a["o"],
+                                                    a["odt"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), mi.ERR_INVALID_ARG),
+    (dict(S=-1), mi.ERR_INVALID_ARG),
+    (dict(num=16), mi.ERR_UNSUPPORTED),
+    (dict(num=-1), mi.ERR_UNSUPPORTED),
+    (dict(tp=3), mi.ERR_UNSUPPORTED),
+    (dict(tp=2048), mi.ERR_UNSUPPORTED),
+    (dict(tp=-4), mi.ERR_UNSUPPORTED),
+    (dict(odt=5), mi.ERR_UNSUPPORTED),
+    (dict(ps=8), mi.ERR_UNSUPPORTED),
+    (dict(D=96), mi.ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), mi.ERR_INVALID_ARG),
+    (dict(scale=0.0), mi.ERR_INVALID_ARG),
+    (dict(S=2, ws=1, wsb=64), mi.ERR_WORKSPACE),
+])
+def test_decode_numerics_validation(kw, code):
+    assert _decn(**kw) == code
+    assert mi.last_error() != ""
+
+
+def test_decode_numerics_empty_batch_is_noop_and_workspace_size():
+    assert _decn(B=0, q=None) == mi.OK
+    n = mi.decode_numerics_workspace_bytes(3, 5, 64, 7)
+    assert n >= 3 * 5 * 7 * 66 * 4 and n % 256 == 0
+    assert mi.decode_numerics_workspace_bytes(3, 5, 64, 1) > 0
+    assert mi.decode_numerics_workspace_bytes(0, 5, 64, 1) == 0
+    for name in ("RECORD_LSE", "RECORD_NUMERATOR_F32", "RECORD_NORMALIZED_BF16", "RECORD_NUMERATOR_BF16",
+                 "NUMERICS_ROUNDED_NORMALIZER", "NUMERICS_P_FP16"):
+        hdr = open(HEADER).read()
+        assert re.search(rf"#define MIATTN_{name}\s+{getattr(mi, name)}\b", hdr), name
