@@ -19,15 +19,18 @@ Forms:
 - ``prefill_paged_dense``: the same materialized form for a chunk of query
   rows against a paged cache holding the whole sequence (queries aligned to
   the end of the sequence for causal masking).
+- ``attention_bwd_dense``: the gradients of the same definition (dQ, dK, dV of
+  sum(dO * O)), with scores recomputed in fp64, for the backward pass.
 - ``attention_brute`` / ``decode_brute``: pure-Python loops with ``math.fsum``
   for tiny inputs and the worked example.
 - ``decode_split_partials`` + ``combine_partials``: the split-into-groups form
   of "Why the calculation is split into groups" with the log-sum-exp merge of
   the FlashAttention 2 style described under "Backend names expand into four
   decode algorithms"; also the combine oracle for arbitrary partials.
-- ``emulate``: fp32/bf16 scalar emulation used only to pin the split geometry
-  and merge formula against the numbers printed under "Plugging in actual
-  numbers".
+- ``emulate``: fp32/bf16 scalar emulation of the four decode programs of "Why
+  your local LLM feels dumber than it is" (their geometries, rounding points and
+  merges), pinned against the numbers printed under "Plugging in actual
+  numbers" and, in exact arithmetic, against the printed exact output.
 
 Every function is pinned by ``tests/test_oracle_*.py`` against values printed
 on the pages (``tests/golden/``), closed forms, special cases, brute force and
@@ -37,6 +40,7 @@ project's design notes.
 from .reference import (  # noqa: F401
     attention_dense,
     attention_brute,
+    attention_bwd_dense,
     attention_rows,
     decode_dense,
     decode_brute,

@@ -87,6 +87,57 @@ def attention_dense(q, k, v, cu_seqlens, num_q_heads: int, num_kv_heads: int,
     return O, LSE
 
 
+def attention_bwd_dense(q, k, v, dout, cu_seqlens, num_q_heads: int, num_kv_heads: int,
+                        scale: float, causal: bool):
+    """Gradients of L = sum(dout * O) for O = attention_dense(q, k, v, ...).
+
+    The backward pass the ELI5 of "Why your local LLM feels dumber than it is"
+    describes recomputes the scores instead of storing them; what it computes
+    is the derivative of the definition above, by the chain rule through
+    s = scale q.k, P = softmax_j(s) and O = P V:
+        dV_j = sum_i P_ij dO_i
+        dP_ij = dO_i . V_j
+        dS_ij = P_ij (dP_ij - sum_k P_ik dP_ik)
+        dQ_i = scale sum_j dS_ij K_j,    dK_j = scale sum_i dS_ij Q_i
+    (masked pairs have P = 0 and contribute nothing). With GQA a kv head's
+    dK/dV sum the contributions of every query head reading it. Scores are
+    recomputed here in fp64 from the inputs; the forward's LSE is not used.
+    Returns dq [T, Hq, D], dk [T, Hkv, D], dv [T, Hkv, D] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    T, Hq, D = q.shape
+    assert Hq == num_q_heads and k.shape[1] == num_kv_heads
+    assert num_q_heads % num_kv_heads == 0
+    group = num_q_heads // num_kv_heads
+    dq = np.zeros_like(q)
+    dk = np.zeros((T, num_kv_heads, D), dtype=np.float64)
+    dv = np.zeros((T, num_kv_heads, v.shape[2]), dtype=np.float64)
+    cu = [int(x) for x in cu_seqlens]
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        L = s1 - s0
+        if L <= 0:
+            continue
+        mask = np.triu(np.ones((L, L), dtype=bool), 1) if causal else None
+        for h in range(Hq):
+            g = h // group
+            Q, K, V, dO = q[s0:s1, h], k[s0:s1, g], v[s0:s1, g], do[s0:s1, h]
+            S = scale * (Q @ K.T)
+            if mask is not None:
+                S[mask] = NEG_INF
+            m = S.max(axis=1, keepdims=True)
+            W = np.exp(S - m)
+            P = W / W.sum(axis=1, keepdims=True)
+            dv[s0:s1, g] += P.T @ dO
+            dP = dO @ V.T
+            dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+            dq[s0:s1, h] = scale * (dS @ K)
+            dk[s0:s1, g] += scale * (dS.T @ Q)
+    return dq, dk, dv
+
+
 def attention_brute(q, k, v, cu_seqlens, num_q_heads: int, num_kv_heads: int,
                     scale: float, causal: bool):
     """The same definition with scalar Python loops and exactly rounded sums

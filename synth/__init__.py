@@ -112,6 +112,14 @@ def make_prefill(cfg: int, seed: int, seqlens, num_q_heads: int, num_kv_heads: i
                        head_dim, float(np.float32(scale)), causal, dtype)
 
 
+def output_gradient(cfg: int, seed: int, total_tokens: int, num_q_heads: int, head_dim: int) -> np.ndarray:
+    """Upstream gradient dO [T, Hq, D] for a backward pass over a prefill case:
+    standard normals from its own stream default_rng([cfg, seed, 2]) (so the
+    case's Q/K/V draws are unchanged), rounded to bf16 bits."""
+    rng = np.random.default_rng([cfg, seed, 2])
+    return bf16_bits(_normal(rng, (total_tokens, num_q_heads, head_dim)))
+
+
 def config1(seed: int = 0, S: int = 256, D: int = 64) -> PrefillCase:
     """Single-head dense fp32 attention, Sq=Sk=256, D=64, non-causal, scale 1/8."""
     return make_prefill(1, seed, [S], 1, 1, D, 0.125, False, "fp32", f"dense_fp32_s{S}_d{D}")

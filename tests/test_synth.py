@@ -53,3 +53,13 @@ def test_worked_example_inputs_are_bf16_exact():
     s, v = synth.worked_example_scores_values()
     assert np.array_equal(synth.bf16_to_f64(synth.bf16_bits(s.astype(np.float32))), s)
     assert np.array_equal(synth.bf16_to_f64(synth.bf16_bits(v.astype(np.float32))), v)
+
+
+def test_output_gradient_stream_is_separate():
+    c = synth.make_prefill(2, 0, [100, 28], 4, 2, 64, 0.125, True)
+    d1 = synth.output_gradient(2, 0, c.total_tokens, 4, 64)
+    d2 = synth.output_gradient(2, 0, c.total_tokens, 4, 64)
+    assert d1.shape == (128, 4, 64) and d1.dtype == np.uint16 and np.array_equal(d1, d2)
+    assert not np.array_equal(d1, c.q)
+    x = synth.bf16_to_f64(d1)
+    assert abs(x.mean()) < 0.05 and abs(x.std() - 1) < 0.05
