@@ -20,7 +20,9 @@ Forms:
   rows against a paged cache holding the whole sequence (queries aligned to
   the end of the sequence for causal masking).
 - ``attention_bwd_dense``: the gradients of the same definition (dQ, dK, dV of
-  sum(dO * O)), with scores recomputed in fp64, for the backward pass.
+  sum(dO * O)), with scores recomputed in fp64, for the backward pass;
+  ``attention_bwd_given``: the same products as a function of the forward's
+  stored output and log-sum-exp, as a recomputing backward receives them.
 - ``attention_brute`` / ``decode_brute``: pure-Python loops with ``math.fsum``
   for tiny inputs and the worked example.
 - ``decode_split_partials`` + ``combine_partials``: the split-into-groups form
@@ -41,6 +43,7 @@ from .reference import (  # noqa: F401
     attention_dense,
     attention_brute,
     attention_bwd_dense,
+    attention_bwd_given,
     attention_rows,
     decode_dense,
     decode_brute,

@@ -138,6 +138,49 @@ def attention_bwd_dense(q, k, v, dout, cu_seqlens, num_q_heads: int, num_kv_head
     return dq, dk, dv
 
 
+def attention_bwd_given(q, k, v, o, lse, dout, cu_seqlens, num_q_heads: int, num_kv_heads: int,
+                        scale: float, causal: bool):
+    """The backward pass as a function of the tensors it is handed: the
+    forward's stored output o and log-sum-exp lse besides q, k, v and dout.
+    The probabilities are rebuilt from lse, P_ij = exp(scale q_i.k_j - lse_i),
+    and the row term from the stored output, Delta_i = dout_i . o_i; then
+    dS = P (dP - Delta) and the same products as attention_bwd_dense. With the
+    exact forward outputs the two functions agree; with o rounded to its
+    storage format (bf16) this is what a recomputing backward computes, and
+    it differs from the exact gradients by the rounding of o.
+    Returns dq [T, Hq, D], dk [T, Hkv, D], dv [T, Hkv, D] float64."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    do = np.asarray(dout, dtype=np.float64)
+    T, Hq, D = q.shape
+    assert Hq == num_q_heads and k.shape[1] == num_kv_heads and lse.shape == (Hq, T)
+    group = num_q_heads // num_kv_heads
+    dq = np.zeros_like(q)
+    dk = np.zeros((T, num_kv_heads, D), dtype=np.float64)
+    dv = np.zeros((T, num_kv_heads, v.shape[2]), dtype=np.float64)
+    cu = [int(x) for x in cu_seqlens]
+    for b in range(len(cu) - 1):
+        s0, s1 = cu[b], cu[b + 1]
+        L = s1 - s0
+        if L <= 0:
+            continue
+        mask = np.triu(np.ones((L, L), dtype=bool), 1) if causal else np.zeros((L, L), dtype=bool)
+        for h in range(Hq):
+            g = h // group
+            Q, K, V, dO, Oh = q[s0:s1, h], k[s0:s1, g], v[s0:s1, g], do[s0:s1, h], o[s0:s1, h]
+            S = scale * (Q @ K.T)
+            P = np.exp(S - lse[h, s0:s1, None])
+            P[mask] = 0.0
+            dv[s0:s1, g] += P.T @ dO
+            dS = P * (dO @ V.T - np.sum(dO * Oh, axis=1, keepdims=True))
+            dq[s0:s1, h] = scale * (dS @ K)
+            dk[s0:s1, g] += scale * (dS.T @ Q)
+    return dq, dk, dv
+
+
 def attention_brute(q, k, v, cu_seqlens, num_q_heads: int, num_kv_heads: int,
                     scale: float, causal: bool):
     """The same definition with scalar Python loops and exactly rounded sums

@@ -92,3 +92,30 @@ def test_closed_forms():
         assert np.all(dq[50] == 0) and np.all(dk[50] == 0)
         for g in range(Hkv):
             assert np.max(np.abs(dv[50, g] - do[50, g * G:(g + 1) * G].sum(axis=0))) < 1e-15
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_given_form_with_exact_forward_outputs_is_the_gradient(causal):
+    seqlens, Hq, Hkv, D, scale = [37, 64, 1, 20], 8, 2, 16, 0.25
+    q, k, v, do, cu = _case(seqlens, Hq, Hkv, D, 3)
+    O, LSE = oracle.attention_dense(q, k, v, cu, Hq, Hkv, scale, causal)
+    want = oracle.attention_bwd_dense(q, k, v, do, cu, Hq, Hkv, scale, causal)
+    got = oracle.attention_bwd_given(q, k, v, O, LSE, do, cu, Hq, Hkv, scale, causal)
+    for w, g in zip(want, got):
+        assert np.max(np.abs(w - g)) < 1e-12
+
+
+def test_given_form_sees_the_stored_output():
+    # shifting the stored output of one row by e moves Delta of that row by
+    # dO . e and changes only that query's dQ and the keys it sees
+    seqlens, Hq, Hkv, D, scale = [12], 2, 1, 4, 0.5
+    q, k, v, do, cu = _case(seqlens, Hq, Hkv, D, 4)
+    O, LSE = oracle.attention_dense(q, k, v, cu, Hq, Hkv, scale, True)
+    O2 = O.copy()
+    O2[5, 1] += 0.25
+    a = oracle.attention_bwd_given(q, k, v, O, LSE, do, cu, Hq, Hkv, scale, True)
+    b = oracle.attention_bwd_given(q, k, v, O2, LSE, do, cu, Hq, Hkv, scale, True)
+    dq_diff = np.abs(a[0] - b[0]).sum(axis=2)
+    assert np.count_nonzero(dq_diff > 1e-15) == 1 and dq_diff[5, 1] > 0
+    assert np.all(a[2] == b[2])                                   # dV does not use Delta
+    assert np.all(np.abs(a[1] - b[1])[6:] < 1e-15)                 # keys after query 5 unaffected
