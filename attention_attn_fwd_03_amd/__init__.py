@@ -14,6 +14,8 @@ Entry points (same names as the C ABI, without the ``miattn_`` prefix):
     attn_decode_paged_numerics(..., *, scale, num_splits, numerics,
                                tile_pages, out_dtype) -> (o, lse)
     attn_combine(partial_o, partial_lse, *, out_dtype) -> (o, lse)
+    attn_bwd(q, k, v, o, lse, dout, cu_seqlens, max_seqlen, *, scale,
+             causal) -> (dq, dk, dv)
 """
 from __future__ import annotations
 
@@ -55,6 +57,10 @@ def _load():
     lib.miattn_attn_decode_paged_numerics.restype = I
     lib.miattn_decode_numerics_workspace_bytes.argtypes = [I, I, I, I]
     lib.miattn_decode_numerics_workspace_bytes.restype = Z
+    lib.miattn_attn_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, Z, P]
+    lib.miattn_attn_bwd.restype = I
+    lib.miattn_attn_bwd_workspace_bytes.argtypes = [I, I]
+    lib.miattn_attn_bwd_workspace_bytes.restype = Z
     lib.miattn_attn_combine.argtypes = [P, P, I, I, I, P, P, I, P]
     lib.miattn_attn_combine.restype = I
     lib.miattn_decode_workspace_bytes.argtypes = [I, I, I, I]
@@ -126,6 +132,37 @@ def attn_fwd(q, k, v, cu_seqlens, max_seqlen: int, *, scale: float, causal: bool
                                _ptr(cu_seqlens), cu_seqlens.numel() - 1, int(max_seqlen), T, Hq, Hkv, D,
                                float(scale), int(bool(causal)), dt, _stream(q.device)))
     return o, (lse if return_lse else None)
+
+
+def attn_bwd_workspace_bytes(total_tokens: int, num_q_heads: int) -> int:
+    return int(lib.miattn_attn_bwd_workspace_bytes(total_tokens, num_q_heads))
+
+
+def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, *, scale: float, causal: bool,
+             dq=None, dk=None, dv=None, workspace=None):
+    """Backward of attn_fwd (bf16). q/o/dout [T,Hq,D], k/v [T,Hkv,D], lse
+    [Hq,T] fp32 from attn_fwd. Returns (dq [T,Hq,D], dk, dv [T,Hkv,D])."""
+    _need_cuda(q, k, v, o, lse, dout, cu_seqlens, dq, dk, dv, workspace)
+    T, Hq, D = q.shape
+    Hkv = k.shape[1]
+    for name, t_ in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout)):
+        if t_.dtype != torch.bfloat16:
+            raise ValueError(f"{name} must be bf16")
+    if k.shape != (T, Hkv, D) or v.shape != (T, Hkv, D) or o.shape != q.shape or dout.shape != q.shape:
+        raise ValueError("shapes do not match")
+    if lse.dtype != torch.float32 or lse.shape != (Hq, T):
+        raise ValueError("lse must be fp32 [Hq, T]")
+    if cu_seqlens.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    dq = dq if dq is not None else torch.empty_like(q)
+    dk = dk if dk is not None else torch.empty_like(k)
+    dv = dv if dv is not None else torch.empty_like(v)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.miattn_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(cu_seqlens),
+                               cu_seqlens.numel() - 1, int(max_seqlen), T, Hq, Hkv, D, float(scale),
+                               int(bool(causal)), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes,
+                               _stream(q.device)))
+    return dq, dk, dv
 
 
 def attn_fwd_paged(q, k_cache, v_cache, block_table, cu_seqlens_q, seq_lens_k, max_seqlen_q: int, *,

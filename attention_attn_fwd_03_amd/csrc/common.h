@@ -33,6 +33,30 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+// Two floats -> packed fp16 pair, round to nearest even.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2 v = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ float f16lo_to_f32(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[0]; }
+__device__ __forceinline__ float f16hi_to_f32(uint32_t w) { return (float)__builtin_bit_cast(f16x2, w)[1]; }
+// Eight bf16 -> eight fp16 (exact for magnitudes in fp16's normal range).
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = pack_f16x2(bf16lo_to_f32(v[i]), bf16hi_to_f32(v[i]));
+  return r;
+}
+__device__ __forceinline__ f16x8 as_f16x8(u32x4 v) { return __builtin_bit_cast(f16x8, v); }
+__device__ __forceinline__ f16x8 as_f16x8(u32x2 a, u32x2 b) {
+  u32x4 v = {a[0], a[1], b[0], b[1]};
+  return __builtin_bit_cast(f16x8, v);
+}
+
 // Value held by lane (lane ^ 32): v_permlane32_swap exchanges the upper half
 // wave's first operand with the lower half's second; passing x twice gives
 // each lane its partner's copy in the element it did not keep.

@@ -96,28 +96,6 @@ struct DecodeSmem {
 
 __device__ __forceinline__ float round_bf16(float x) { return bf16lo_to_f32(pack_bf16x2(x, 0.f)); }
 
-typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-
-// Two floats -> packed fp16 pair, round to nearest even.
-__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
-  f16x2 v = {(_Float16)lo, (_Float16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ float f16lo_to_f32(uint32_t w) {
-  return (float)__builtin_bit_cast(f16x2, w)[0];
-}
-__device__ __forceinline__ float f16hi_to_f32(uint32_t w) {
-  return (float)__builtin_bit_cast(f16x2, w)[1];
-}
-// Eight bf16 -> eight fp16 (exact for magnitudes in fp16's normal range).
-__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) r[i] = pack_f16x2(bf16lo_to_f32(v[i]), bf16hi_to_f32(v[i]));
-  return r;
-}
-
 // PF = pages each wave keeps in flight (register double buffering when 2).
 template <int D>
 constexpr int decode_prefetch() { return D >= 256 ? 1 : 2; }

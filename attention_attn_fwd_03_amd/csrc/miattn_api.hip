@@ -11,6 +11,7 @@
 #include <mutex>
 #include <string>
 
+#include "backward.h"
 #include "combine.h"
 #include "decode.h"
 #include "prefill.h"
@@ -460,6 +461,83 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
     if (r) return r;
   }
   return ok();
+}
+
+size_t miattn_attn_bwd_workspace_bytes(int total_tokens, int num_q_heads) {
+  if (total_tokens <= 0 || num_q_heads <= 0) return 0;
+  const size_t bytes = (size_t)total_tokens * num_q_heads * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
+                    const int32_t* cu_seqlens, int num_seqs, int max_seqlen, int total_tokens, int num_q_heads,
+                    int num_kv_heads, int head_dim, float scale, int causal, void* dq, void* dk, void* dv,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "attn_bwd";
+  if (num_seqs < 0 || max_seqlen < 0 || total_tokens < 0) return fail(MIATTN_ERR_INVALID_ARG, "%s: negative size", who);
+  if (num_seqs == 0 || total_tokens == 0) return ok();
+  if (!q || !k || !v || !o || !dout || !lse || !cu_seqlens || !dq || !dk || !dv)
+    return fail(MIATTN_ERR_INVALID_ARG, "%s: null pointer", who);
+  if (max_seqlen <= 0) return fail(MIATTN_ERR_INVALID_ARG, "%s: max_seqlen must be > 0", who);
+  if (num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads != 0)
+    return fail(MIATTN_ERR_INVALID_ARG, "%s: need Hq > 0, Hkv > 0 and Hq %% Hkv == 0", who);
+  if (causal != 0 && causal != 1) return fail(MIATTN_ERR_INVALID_ARG, "%s: causal must be 0 or 1", who);
+  if (!scale_ok(scale)) return fail(MIATTN_ERR_INVALID_ARG, "%s: scale must be finite and > 0", who);
+  if (head_dim != 64 && head_dim != 128) return fail(MIATTN_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128", who);
+  const int G = num_q_heads / num_kv_heads;
+  if (!(G == 1 || G == 2 || G % 4 == 0))
+    return fail(MIATTN_ERR_UNSUPPORTED, "%s: Hq/Hkv must be 1, 2 or a multiple of 4", who);
+  if ((long)total_tokens * num_q_heads * head_dim > 0x7fffffffL)
+    return fail(MIATTN_ERR_INVALID_ARG, "%s: tensors above 2^31 elements are not supported", who);
+  const size_t need = miattn_attn_bwd_workspace_bytes(total_tokens, num_q_heads);
+  if (workspace != nullptr && workspace_bytes < need)
+    return fail(MIATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", who, workspace_bytes, need);
+  const int dev = current_device();
+  if (dev < 0) return dev;
+  hipStream_t st = (hipStream_t)stream;
+  void* ws = workspace;
+  if (ws == nullptr) {
+    const int r = library_workspace(dev, need, &ws, who);
+    if (r) return r;
+  }
+  miattn::BwdArgs a{};
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.o = (const uint16_t*)o; a.dout = (const uint16_t*)dout; a.lse = lse; a.delta = (float*)ws;
+  a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
+  a.cu_seqlens = cu_seqlens; a.num_seqs = num_seqs; a.total_tokens = total_tokens;
+  a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
+  a.heads_per_wg = G >= 4 ? 4 : G;
+  a.n_head_slots = num_kv_heads * (G / a.heads_per_wg);
+  a.c = scale * miattn::kLog2e;
+  a.scale = scale;
+  const long rows = (long)total_tokens * num_q_heads;
+  const int rpb = 256 / (head_dim / 8);
+  const unsigned g_delta = (unsigned)((rows + rpb - 1) / rpb);
+  const unsigned g_dkdv = (unsigned)((long)num_kv_heads * ((max_seqlen + 127) / 128) * num_seqs);
+  const int QR = 32 * (4 / a.heads_per_wg);
+  const unsigned g_dq = (unsigned)((long)a.n_head_slots * ((max_seqlen + QR - 1) / QR) * num_seqs);
+  const dim3 blk(256);
+  if (head_dim == 64) {
+    hipLaunchKernelGGL(miattn::miattn_bwd_delta_kernel<64>, dim3(g_delta), blk, 0, st, a);
+    if (causal) {
+      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<64, true>), dim3(g_dkdv), blk, 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<64, 2, true>), dim3(g_dq), blk, 0, st, a);
+    } else {
+      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<64, false>), dim3(g_dkdv), blk, 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<64, 2, false>), dim3(g_dq), blk, 0, st, a);
+    }
+  } else {
+    hipLaunchKernelGGL(miattn::miattn_bwd_delta_kernel<128>, dim3(g_delta), blk, 0, st, a);
+    if (causal) {
+      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<128, true>), dim3(g_dkdv), blk, 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<128, 2, true>), dim3(g_dq), blk, 0, st, a);
+    } else {
+      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<128, false>), dim3(g_dkdv), blk, 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<128, 2, false>), dim3(g_dq), blk, 0, st, a);
+    }
+  }
+  const int r = check_launch(who);
+  return r ? r : ok();
 }
 
 size_t miattn_decode_numerics_workspace_bytes(int batch, int num_q_heads, int head_dim, int num_splits) {

@@ -244,6 +244,37 @@ int miattn_attn_decode_paged_numerics(const void* q, const void* k_cache, const 
  * batch * Hq * num_splits * (head_dim + 2) floats, rounded up to 256. */
 size_t miattn_decode_numerics_workspace_bytes(int batch, int num_q_heads, int head_dim, int num_splits);
 
+/*
+ * miattn_attn_bwd -- gradients of attention (the operation of miattn_attn_fwd,
+ * bf16) with respect to q, k and v for an upstream gradient dout, by
+ * recomputation: the scores are rebuilt tile by tile from q, k and the
+ * forward's log-sum-exp, as the backward pass of "Why your local LLM feels
+ * dumber than it is" (its ELI5) describes, instead of being stored:
+ *     P = exp(scale q.k - LSE),  dV = P^T dO,  dP = dO V^T,
+ *     dS = P (dP - rowsum(dO o O)),  dQ = scale dS K,  dK = scale dS^T Q.
+ * With GQA, dK/dV of a kv head sum the contributions of all its query heads.
+ *   q, o, dout [total_tokens, Hq, D] bf16; k, v [total_tokens, Hkv, D] bf16;
+ *   lse [Hq, total_tokens] float32 as written by miattn_attn_fwd for the same
+ *   q, k, v (o likewise); cu_seqlens, num_seqs, max_seqlen, scale, causal as
+ *   for miattn_attn_fwd.
+ *   dq [total_tokens, Hq, D], dk, dv [total_tokens, Hkv, D] bf16 (written).
+ *   head_dim 64 or 128; Hq/Hkv 1, 2 or a multiple of 4 (MIATTN_ERR_UNSUPPORTED
+ *   otherwise).
+ *   workspace: miattn_attn_bwd_workspace_bytes bytes of device scratch (the
+ *   fp32 row sums of dO o O), or NULL for the library-owned buffer.
+ * Deterministic: fixed reduction orders, no atomics; dQ is computed by its own
+ * pass over the keys rather than accumulated across workgroups.
+ */
+int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, const int32_t* cu_seqlens, int num_seqs, int max_seqlen,
+                    int total_tokens, int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                    int causal, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* Bytes of workspace miattn_attn_bwd needs: total_tokens * Hq floats,
+ * rounded up to 256 (0 for an empty problem). */
+size_t miattn_attn_bwd_workspace_bytes(int total_tokens, int num_q_heads);
+
 /* Split count chosen for num_splits == 0: the candidate set and efficiency of
  * miattn_split_heuristic with this library's MI355X capacity (256 compute
  * units, one decode workgroup each), 16-token pages as blocks, work units =

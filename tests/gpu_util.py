@@ -47,6 +47,25 @@ def assert_bf16_rounding_of(got, want, slop=2e-5, what=""):
     assert not bad.any(), what
 
 
+def half_ulp_bf16(x):
+    """Half the spacing of bf16 numbers at |x| (the most a correctly rounded
+    bf16 result can differ from x)."""
+    a = np.abs(x)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, np.exp2(e - 8), 0.0)
+
+
+def assert_bf16_close_beyond_rounding(got, want, what=""):
+    """The bf16 bar applied to what a bf16 output can reach: the error beyond
+    each element's own rounding to bf16 (half an ulp of the exact value) within
+    max-abs 1e-2, and the plain error within mean-abs 1e-3."""
+    err = np.abs(got - want)
+    excess = float(np.max(err - half_ulp_bf16(want))) if err.size else 0.0
+    mx, mean = errors(got, want)
+    print(f"  {what}: max-abs {mx:.3e} (beyond rounding {excess:.3e}) mean-abs {mean:.3e}", flush=True)
+    assert excess <= BF16_MAX_ABS and mean <= BF16_MEAN_ABS, (what, mx, excess, mean)
+
+
 def assert_lse_close(got, want, what="", tol=LSE_MAX_ABS):
     fin = np.isfinite(want)
     assert np.array_equal(np.isfinite(got), fin), what

@@ -276,3 +276,39 @@ def test_decode_numerics_empty_batch_is_noop_and_workspace_size():
                  "NUMERICS_ROUNDED_NORMALIZER", "NUMERICS_P_FP16"):
         hdr = open(HEADER).read()
         assert re.search(rf"#define MIATTN_{name}\s+{getattr(mi, name)}\b", hdr), name
+
+
+def _bwd(**kw):
+    a = dict(q=1, k=1, v=1, o=1, do=1, lse=1, cu=1, n=1, maxs=16, T=16, Hq=4, Hkv=2, D=128, scale=0.1,
+             causal=1, dq=1, dk=1, dv=1, ws=None, wsb=0)
+    a.update(kw)
+    return mi.lib.miattn_attn_bwd(a["q"], a["k"], a["v"], a["o"], a["do"], a["lse"], a["cu"], a["n"], a["maxs"],
+                                  a["T"], a["Hq"], a["Hkv"], a["D"], a["scale"], a["causal"], a["dq"], a["dk"],
+                                  a["dv"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), mi.ERR_INVALID_ARG),
+    (dict(lse=None), mi.ERR_INVALID_ARG),
+    (dict(do=None), mi.ERR_INVALID_ARG),
+    (dict(dv=None), mi.ERR_INVALID_ARG),
+    (dict(maxs=0), mi.ERR_INVALID_ARG),
+    (dict(T=-1), mi.ERR_INVALID_ARG),
+    (dict(Hq=6, Hkv=4), mi.ERR_INVALID_ARG),
+    (dict(causal=2), mi.ERR_INVALID_ARG),
+    (dict(scale=float("nan")), mi.ERR_INVALID_ARG),
+    (dict(D=256), mi.ERR_UNSUPPORTED),
+    (dict(D=96), mi.ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=2), mi.ERR_UNSUPPORTED),
+    (dict(ws=1, wsb=16), mi.ERR_WORKSPACE),
+])
+def test_bwd_validation(kw, code):
+    assert _bwd(**kw) == code
+    assert mi.last_error() != ""
+
+
+def test_bwd_empty_is_noop_and_workspace_size():
+    assert _bwd(n=0, q=None) == mi.OK
+    assert _bwd(T=0, q=None) == mi.OK
+    assert mi.attn_bwd_workspace_bytes(100, 3) == 1280
+    assert mi.attn_bwd_workspace_bytes(0, 3) == 0
