@@ -59,7 +59,7 @@ def _load():
     lib.miattn_decode_numerics_workspace_bytes.restype = Z
     lib.miattn_attn_bwd.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, P, P, P, P, Z, P]
     lib.miattn_attn_bwd.restype = I
-    lib.miattn_attn_bwd_workspace_bytes.argtypes = [I, I]
+    lib.miattn_attn_bwd_workspace_bytes.argtypes = [I, I, I, I]
     lib.miattn_attn_bwd_workspace_bytes.restype = Z
     lib.miattn_attn_combine.argtypes = [P, P, I, I, I, P, P, I, P]
     lib.miattn_attn_combine.restype = I
@@ -134,8 +134,8 @@ def attn_fwd(q, k, v, cu_seqlens, max_seqlen: int, *, scale: float, causal: bool
     return o, (lse if return_lse else None)
 
 
-def attn_bwd_workspace_bytes(total_tokens: int, num_q_heads: int) -> int:
-    return int(lib.miattn_attn_bwd_workspace_bytes(total_tokens, num_q_heads))
+def attn_bwd_workspace_bytes(total_tokens: int, num_q_heads: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(lib.miattn_attn_bwd_workspace_bytes(total_tokens, num_q_heads, num_kv_heads, head_dim))
 
 
 def attn_bwd(q, k, v, o, lse, dout, cu_seqlens, max_seqlen: int, *, scale: float, causal: bool,

@@ -9,29 +9,30 @@
 //     dQ_i = scale sum_j dS_ij K_j,      dK_j = scale sum_i dS_ij Q_i.
 // Three kernels, all with fixed reduction orders (bitwise reproducible, no
 // atomics):
-//  * delta: Delta = rowsum(dO * O) in fp32, one pass over O and dO.
-//  * dK/dV: one workgroup of 4 waves per (kv head, 128 keys, sequence); each
-//    wave keeps its 32 keys' K and V as MFMA operands in registers and its
-//    dK^T, dV^T in accumulators, while tiles of 32 queries of Q and dO (for
-//    every query head of the group, so GQA sums stay in registers) stream
-//    through LDS by direct HBM->LDS copies, double-buffered. Per tile:
-//    S = Q K^T and dP = dO V^T (query rows, key columns), then
-//    dV^T += dO^T P and dK^T += Q^T dS: the accumulator registers of P and dS,
-//    rounded to fp16, are the B operand as they stand; dO^T and Q^T come from
-//    the same LDS tile through the transposing read.
+//  * prep: Delta = rowsum(dO * O) in fp32, the LSE in log2 units (both in
+//    rows padded by 32 so tile-sized copies stay in bounds), and fp16 copies
+//    of Q, dO, K and V, in one pass over the inputs.
+//  * dK/dV: one workgroup of 4 waves per (kv head, 32 keys, sequence). Every
+//    wave holds the same 32 keys' K and V as MFMA operands and dK^T, dV^T
+//    accumulators in registers, and takes every fourth (query head, 32-query
+//    tile) step of the group, with its own double-buffered Q/dO tiles copied
+//    straight from HBM into LDS; the waves never wait for each other until the
+//    end, where their four partial sums are added through LDS in a fixed
+//    order. Per tile: S = Q K^T and dP = dO V^T (query rows, key columns),
+//    then dV^T += dO^T P and dK^T += Q^T dS: the accumulator registers of P
+//    and dS, rounded to fp16, are the B operand as they stand; dO^T and Q^T
+//    come from the same LDS tile through the transposing read.
 //  * dQ: the forward's orientation: one wave per 32 query rows of one head,
 //    S^T = K Q^T and dP^T = V dO^T with Q, dO held as operands, K/V tiles
 //    streaming through LDS, dQ^T += K^T dS^T with K^T read transposed.
 // dQ is not accumulated inside the dK/dV kernel, which would need atomics or
 // an ordering between workgroups: the dQ kernel recomputes S and dP instead
 // (7 products per key/query pair instead of 5).
-// Operands are fp16, not bf16: each lane converts the 16 bytes its own direct
-// copy wrote once the copy has landed (before the barrier that publishes the
-// tile), and register operands once at the start. The bf16 inputs convert
-// exactly (inside fp16's range); P and dS are then rounded to fp16 (11
-// significant bits) instead of bf16 (8) for the three gradient products. The
-// gradients are unbounded sums of such products, and with bf16 P and dS their
-// error alone exceeds the bf16 output bar for magnitudes above ~2.
+// Operands are fp16, not bf16: the bf16 inputs convert exactly (inside fp16's
+// range), and P and dS then round to fp16 (11 significant bits) instead of
+// bf16 (8) for the three gradient products. The gradients are unbounded sums
+// of such products; with bf16 P and dS their rounding alone exceeds the bf16
+// output bar for magnitudes above ~2.
 #pragma once
 #include <type_traits>
 
@@ -40,37 +41,41 @@
 namespace miattn {
 
 struct BwdArgs {
-  const uint16_t* q;          // [T, Hq, D]
-  const uint16_t* k;          // [T, Hkv, D]
+  const uint16_t* q;          // [T, Hq, D] bf16
+  const uint16_t* k;          // [T, Hkv, D] bf16
   const uint16_t* v;
-  const uint16_t* o;          // [T, Hq, D] forward output
-  const uint16_t* dout;       // [T, Hq, D]
+  const uint16_t* o;          // [T, Hq, D] forward output, bf16
+  const uint16_t* dout;       // [T, Hq, D] bf16
   const float* lse;           // [Hq, T] forward log-sum-exp (natural log)
-  float* delta;               // [Hq, T] workspace
-  uint16_t* dq;               // [T, Hq, D]
-  uint16_t* dk;               // [T, Hkv, D]
+  float* stats;               // workspace [2][Hq][t_pad]: LSE in log2 units, Delta
+  uint16_t* q16;              // workspace fp16 copies: [T, Hq, D]
+  uint16_t* do16;             // [T, Hq, D]
+  uint16_t* k16;              // [T, Hkv, D]
+  uint16_t* v16;              // [T, Hkv, D]
+  uint16_t* dq;               // [T, Hq, D] bf16
+  uint16_t* dk;               // [T, Hkv, D] bf16
   uint16_t* dv;
   const int32_t* cu_seqlens;  // [num_seqs + 1]
   int num_seqs;
   int total_tokens;
+  int t_pad;                  // row length of the stats arrays (>= T + 32)
   int num_q_heads;
   int num_kv_heads;
   int group;                  // G
   int heads_per_wg;           // dQ kernel: query heads per workgroup (NH)
-  int n_units;                // grid units per sequence (key blocks or query tiles)
   int n_head_slots;           // dQ kernel: Hkv * G / NH
   float c;                    // scale * log2(e)
   float scale;
 };
 
-// LDS tile of R rows x D bf16 read both ways: as a 128-bit operand (16
-// consecutive rows x one 16-byte chunk per cycle) and through the transposing
-// read (4 consecutive rows x 4 consecutive chunks per cycle). Chunk c of row
-// r sits in slot c ^ swz(r). D >= 128 (16+ slots per row, one row per 64
-// banks): swz = 4 (r mod 4) + (r / 4) mod 4 gives 16 consecutive rows 16
-// different slots, and 4 consecutive rows 4 different groups of 4 slots.
-// D = 64 (two rows per 64 banks): the same on r / 2, with the parity of r
-// choosing the half of the banks.
+// LDS tile of R rows x D 16-bit values read both ways: as a 128-bit operand
+// (16 consecutive rows x one 16-byte chunk per cycle) and through the
+// transposing read (4 consecutive rows x 4 consecutive chunks per cycle).
+// Chunk c of row r sits in slot c ^ swz(r). D >= 128 (16+ slots per row, one
+// row per 64 banks): swz = 4 (r mod 4) + (r / 4) mod 4 gives 16 consecutive
+// rows 16 different slots, and 4 consecutive rows 4 different groups of 4
+// slots. D = 64 (two rows per 64 banks): the same on r / 2, with the parity
+// of r choosing the half of the banks.
 template <int D>
 struct BwdTile {
   static constexpr int CH = D / 8;
@@ -79,40 +84,52 @@ struct BwdTile {
   }
 };
 
-// ---------------------------------------------------------------- delta
-// One row (token, head) per CH = D/8 lanes; 16-byte loads of O and dO, fp32
-// products, an xor-tree over the CH lanes.
+// Forward log-sum-exp in log2 units of the raw score times c; a row that saw
+// no key (-inf) gives +inf, i.e. P = 0.
+__device__ __forceinline__ float lse_to_log2(float lse) {
+  return lse == kNegInf ? __builtin_inff() : lse * kLog2e;
+}
+
+// ---------------------------------------------------------------- prep
+// Rows (token, query head) give Delta = dO . O in fp32, the LSE in log2 units
+// and fp16 copies of Q and dO; rows (token, kv head) give fp16 copies of K and
+// V. CH = D/8 lanes per row, 16 bytes each; a row group never straddles the
+// two ranges' boundary branch (the branch is uniform over the CH lanes).
 template <int D>
-__global__ __launch_bounds__(256) void miattn_bwd_delta_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256) void miattn_bwd_prep_kernel(BwdArgs a) {
   constexpr int CH = D / 8;
   constexpr int RPB = 256 / CH;
   const int t = threadIdx.x;
-  const long row = (long)blockIdx.x * RPB + t / CH;   // token * Hq + head
-  const long rows = (long)a.total_tokens * a.num_q_heads;
+  const long row = (long)blockIdx.x * RPB + t / CH;
+  const long rq = (long)a.total_tokens * a.num_q_heads;
+  const long rk = (long)a.total_tokens * a.num_kv_heads;
   const int ch = t % CH;
-  float acc = 0.f;
-  if (row < rows) {
-    const u32x4 ov = ld16(a.o + row * D + 8 * ch);
-    const u32x4 dv = ld16(a.dout + row * D + 8 * ch);
+  if (row < rq) {
+    const size_t e = (size_t)row * D + 8 * ch;
+    const u32x4 ov = ld16(a.o + e);
+    const u32x4 dv = ld16(a.dout + e);
+    st16(a.q16 + e, bf16x8_to_f16x8(ld16(a.q + e)));
+    st16(a.do16 + e, bf16x8_to_f16x8(dv));
+    float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       acc += bf16lo_to_f32(ov[i]) * bf16lo_to_f32(dv[i]);
       acc += bf16hi_to_f32(ov[i]) * bf16hi_to_f32(dv[i]);
     }
-  }
 #pragma unroll
-  for (int m = CH / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, CH);
-  if (row < rows && ch == 0) {
-    const long tok = row / a.num_q_heads;
-    const int h = (int)(row % a.num_q_heads);
-    a.delta[(size_t)h * a.total_tokens + tok] = acc;
+    for (int m = CH / 2; m > 0; m >>= 1) acc += __shfl_xor(acc, m, CH);
+    if (ch == 0) {
+      const long tok = row / a.num_q_heads;
+      const int h = (int)(row % a.num_q_heads);
+      const size_t si = (size_t)h * a.t_pad + tok;
+      a.stats[si] = lse_to_log2(a.lse[(size_t)h * a.total_tokens + tok]);
+      a.stats[(size_t)a.num_q_heads * a.t_pad + si] = acc;
+    }
+  } else if (row < rq + rk) {
+    const size_t e = (size_t)(row - rq) * D + 8 * ch;
+    st16(a.k16 + e, bf16x8_to_f16x8(ld16(a.k + e)));
+    st16(a.v16 + e, bf16x8_to_f16x8(ld16(a.v + e)));
   }
-}
-
-// Forward log-sum-exp in log2 units of the raw score times c; a row that saw
-// no key (-inf) gives +inf, i.e. P = 0.
-__device__ __forceinline__ float lse_to_log2(float lse) {
-  return lse == kNegInf ? __builtin_inff() : lse * kLog2e;
 }
 
 // ---------------------------------------------------------------- dK / dV
@@ -123,15 +140,19 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
   constexpr int NKK = D / 16;                        // MFMA steps over the head dim
   constexpr int NDT = D / 32;                        // 32-wide d blocks of dK^T / dV^T
   constexpr int QT = 32;                             // queries per tile
-  constexpr int TILE_BYTES = QT * D * 2;
-  constexpr int NI = TILE_BYTES / 1024 / 4;          // 1-KB copies per wave per tensor
-  static_assert(TILE_BYTES % 4096 == 0, "tile must split into 1-KB copies over 4 waves");
-  __shared__ __attribute__((aligned(1024))) uint8_t q_lds0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t q_lds1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t d_lds0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t d_lds1[TILE_BYTES];
-  auto qbuf = [&](int i) { return (MIATTN_LDS uint8_t*)(i == 0 ? q_lds0 : q_lds1); };
-  auto dbuf = [&](int i) { return (MIATTN_LDS uint8_t*)(i == 0 ? d_lds0 : d_lds1); };
+  constexpr int TILE = QT * D * 2;                   // bytes of one Q or dO tile
+  constexpr int NC = TILE / 1024;                    // 1-KB copies per tensor and tile
+  static_assert(TILE % 1024 == 0, "tile must split into 1-KB copies");
+  static_assert(2 * QT * D * 4 <= 4 * TILE, "two waves' fp32 partials must fit one tile array");
+  // wave w owns bytes [w TILE, (w+1) TILE) of each array; four separate LDS
+  // objects so that a copy in flight into one buffer does not hold up reads
+  // of the other
+  __shared__ __attribute__((aligned(1024))) uint8_t q_lds0[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t q_lds1[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t d_lds0[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t d_lds1[4 * TILE];
+  __shared__ __attribute__((aligned(16))) float st_lds0[4 * 64];   // per wave: 32 LSE, 32 Delta
+  __shared__ __attribute__((aligned(16))) float st_lds1[4 * 64];
 
   // work item: (kv head, key block, sequence), kv head fastest; key block 0
   // (the most causal work) first
@@ -145,7 +166,7 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
   s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
   s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
   const int L = s1 - s0;
-  const int kb0 = kblk * 128;
+  const int kb0 = kblk * 32;
   if (kb0 >= L) return;   // uniform over the workgroup
 
   const int lane = threadIdx.x & 63;
@@ -154,85 +175,69 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
   const int bb = lane >> 4, kq = lane & 15;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = a.group;
   const float c = a.c;
-  const int key = kb0 + 32 * wave + (lane & 31);     // this lane's key column
+  const int key = kb0 + (lane & 31);                 // this lane's key column
   const bool key_ok = key < L;
 
-  // K, V of the wave's 32 keys as B operands: lane holds key lane%32,
-  // d = 16 kk + 8 half + 0..7
+  MIATTN_LDS uint8_t* qb[2] = {(MIATTN_LDS uint8_t*)q_lds0 + wave * TILE, (MIATTN_LDS uint8_t*)q_lds1 + wave * TILE};
+  MIATTN_LDS uint8_t* db[2] = {(MIATTN_LDS uint8_t*)d_lds0 + wave * TILE, (MIATTN_LDS uint8_t*)d_lds1 + wave * TILE};
+  MIATTN_LDS float* sb[2] = {(MIATTN_LDS float*)st_lds0 + wave * 64, (MIATTN_LDS float*)st_lds1 + wave * 64};
+
+  // K, V of the 32 keys as B operands: lane holds key lane%32,
+  // d = 16 kk + 8 half + 0..7 (fp16 copies)
   u32x4 kop[NKK], vop[NKK];
   {
     const size_t off = ((size_t)(s0 + (key_ok ? key : 0)) * Hkv + g) * D + 8 * half;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const u32x4 z = {0u, 0u, 0u, 0u};
-      kop[kk] = key_ok ? bf16x8_to_f16x8(ld16(a.k + off + 16 * kk)) : z;
-      vop[kk] = key_ok ? bf16x8_to_f16x8(ld16(a.v + off + 16 * kk)) : z;
+      kop[kk] = key_ok ? ld16(a.k16 + off + 16 * kk) : z;
+      vop[kk] = key_ok ? ld16(a.v16 + off + 16 * kk) : z;
     }
   }
 
-  // query tiles: causal tiles start at the one holding query kb0
+  // steps: (query head of the group, query tile); causal tiles start at the
+  // one holding query kb0; this wave takes steps wave, wave + 4, ...
   const int n_qt = (L + QT - 1) / QT;
   const int qt0 = CAUSAL ? kb0 / QT : 0;
   const int nq = n_qt - qt0;
   const int n_steps = G * nq;
+  const int n_mine = n_steps > wave ? (n_steps - wave + 3) / 4 : 0;
 
-  // copies of tile (head h, query tile qt): lane i of copy j fills slot
-  // lidx % CH of row lidx / CH with the chunk the swizzle maps there; rows
-  // past the sequence end repeat its last row (their P is masked to 0)
+  // copy j of a tile: lane fills slot lidx % CH of row lidx / CH (lidx =
+  // 64 j + lane) with the chunk the swizzle maps there; rows past the
+  // sequence end repeat its last row (their P and dS are masked to 0)
   const size_t q_row = (size_t)Hq * D;
-  uint32_t qoff[NI];
+  uint32_t qoff[NC];
 #pragma unroll
-  for (int j = 0; j < NI; ++j) {
-    const int lidx = (wave * NI + j) * 64 + lane;
+  for (int j = 0; j < NC; ++j) {
+    const int lidx = j * 64 + lane;
     const int r = lidx / CH;
     const int slot = lidx % CH;
     qoff[j] = (uint32_t)(((size_t)r * q_row + 8 * (slot ^ TL::swz(r))) * 2);
   }
-  auto step_head = [&](int st) { return g * G + st / nq; };
-  auto step_tile = [&](int st) { return qt0 + st % nq; };
-  auto load_tile = [&](int st, int buf) {
-    const int h = step_head(st);
-    const int q0 = step_tile(st) * QT;
+  // LSE (lanes 0-7) and Delta (lanes 8-15) of the tile's 32 rows: 16 bytes
+  // each from the padded stats rows
+  const uint32_t st_lane = (uint32_t)(((lane >= 8 ? (size_t)Hq * a.t_pad : 0) + 4 * (lane & 7)) * 4);
+  auto load_tile = [&](int i, int buf) {
+    const int st = wave + 4 * i;
+    const int h = g * G + st / nq;
+    const int q0 = (qt0 + st % nq) * QT;
     const bool full = q0 + QT <= L;
-    const char* qb0 = (const char*)(a.q + ((size_t)(s0 + q0) * Hq + h) * D);
-    const char* db0 = (const char*)(a.dout + ((size_t)(s0 + q0) * Hq + h) * D);
+    const char* qsrc = (const char*)(a.q16 + ((size_t)(s0 + q0) * Hq + h) * D);
+    const char* dsrc = (const char*)(a.do16 + ((size_t)(s0 + q0) * Hq + h) * D);
 #pragma unroll
-    for (int j = 0; j < NI; ++j) {
+    for (int j = 0; j < NC; ++j) {
       uint32_t off = qoff[j];
       if (!full) {
-        const int r = ((wave * NI + j) * 64 + lane) / CH;
+        const int r = (j * 64 + lane) / CH;
         const int rr = q0 + r < L ? r : L - 1 - q0;
         off -= (uint32_t)((size_t)(r - rr) * q_row * 2);
       }
-      dma16_to_lds(qb0, off, qbuf(buf) + (wave * NI + j) * 1024);
-      dma16_to_lds(db0, off, dbuf(buf) + (wave * NI + j) * 1024);
+      dma16_to_lds(qsrc, off, qb[buf] + j * 1024);
+      dma16_to_lds(dsrc, off, db[buf] + j * 1024);
     }
-  };
-  // bf16 -> fp16 in place, on the 16 bytes this lane's copies wrote; the
-  // copies must have landed (vmcnt(0)), the barrier after publishes the tile
-  auto convert_own = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      MIATTN_LDS uint8_t* pq = qbuf(buf) + (wave * NI + j) * 1024 + 16 * lane;
-      MIATTN_LDS uint8_t* pd = dbuf(buf) + (wave * NI + j) * 1024 + 16 * lane;
-      lds_st16(pq, bf16x8_to_f16x8(lds_ld16(pq)));
-      lds_st16(pd, bf16x8_to_f16x8(lds_ld16(pd)));
-    }
-  };
-  // log2-unit LSE and Delta of the 16 query rows a lane's S elements belong
-  // to: rows 8 (i/4) + 4 half + i%4 of the tile
-  auto load_stats = [&](int st, float* l2, float* dl) {
-    const int h = step_head(st);
-    const int q0 = step_tile(st) * QT;
-    const float* lp = a.lse + (size_t)h * a.total_tokens + s0;
-    const float* dp = a.delta + (size_t)h * a.total_tokens + s0;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int row = q0 + 8 * (i >> 2) + 4 * half + (i & 3);
-      row = row < L ? row : L - 1;
-      l2[i] = lse_to_log2(lp[row]);
-      dl[i] = dp[row];
-    }
+    if (lane < 16)
+      dma16_to_lds(a.stats, st_lane + (uint32_t)(((size_t)h * a.t_pad + s0 + q0) * 4), sb[buf]);
   };
 
   f32x16 dk_acc[NDT], dv_acc[NDT];
@@ -244,21 +249,28 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
       dv_acc[i][r] = 0.f;
     }
 
-  float l2[16], dl[16];
-  if (n_steps > 0) {
-    load_tile(0, 0);
-    load_stats(0, l2, dl);
-  }
+  if (n_mine > 0) load_tile(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (n_steps > 0) convert_own(0);
-  __syncthreads();
 
-  auto step = [&](int st, auto bufc) {
+  auto step = [&](int i, auto bufc) {
     constexpr int buf = decltype(bufc)::value;
-    if (st + 1 < n_steps) load_tile(st + 1, buf ^ 1);
-    const MIATTN_LDS uint8_t* ql = qbuf(buf);
-    const MIATTN_LDS uint8_t* dl_ = dbuf(buf);
-    const int q0 = step_tile(st) * QT;
+    if (i + 1 < n_mine) load_tile(i + 1, buf ^ 1);
+    const MIATTN_LDS uint8_t* ql = qb[buf];
+    const MIATTN_LDS uint8_t* dl_ = db[buf];
+    const int st = wave + 4 * i;
+    const int q0 = (qt0 + st % nq) * QT;
+    // this lane's 16 rows: 8 (e/4) + 4 half + e%4
+    float l2[16], dl[16];
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const f32x4 lv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sb[buf] + 8 * gi + 4 * half);
+      const f32x4 dv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sb[buf] + 32 + 8 * gi + 4 * half);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        l2[4 * gi + e] = lv[e];
+        dl[4 * gi + e] = dv[e];
+      }
+    }
     // S = Q K^T and dP = dO V^T: A = row lane%32 of the tile, chunk 2 kk + half
     f32x16 s, dp;
 #pragma unroll
@@ -275,23 +287,23 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
         dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(lds_ld16(dl_ + so)), as_f16x8(vop[kk]), dp, 0, 0, 0);
       }
     }
-    // P = exp2(s c - lse2) and dS = P (dP - Delta), masked to 0 outside the
+    // P = exp2(s c - lse2) and dS = P (dP - Delta), both 0 outside the
     // sequence and (causal) above the diagonal
     u32x4 pw[2], dsw[2];
 #pragma unroll
-    for (int i = 0; i < 16; i += 2) {
+    for (int e0 = 0; e0 < 16; e0 += 2) {
       float p[2], d[2];
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int qrow = q0 + 8 * ((i + e) >> 2) + 4 * half + ((i + e) & 3);
+      for (int u = 0; u < 2; ++u) {
+        const int e = e0 + u;
+        const int qrow = q0 + 8 * (e >> 2) + 4 * half + (e & 3);
         const bool ok = key_ok && qrow < L && (!CAUSAL || key <= qrow);
-        p[e] = ok ? exp2_hw(__builtin_fmaf(s[i + e], c, -l2[i + e])) : 0.f;
-        d[e] = p[e] * (dp[i + e] - dl[i + e]);
+        p[u] = ok ? exp2_hw(__builtin_fmaf(s[e], c, -l2[e])) : 0.f;
+        d[u] = ok ? p[u] * (dp[e] - dl[e]) : 0.f;
       }
-      pw[i >> 3][(i >> 1) & 3] = pack_f16x2(p[0], p[1]);
-      dsw[i >> 3][(i >> 1) & 3] = pack_f16x2(d[0], d[1]);
+      pw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(p[0], p[1]);
+      dsw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(d[0], d[1]);
     }
-    if (st + 1 < n_steps) load_stats(st + 1, l2, dl);
     // dV^T += dO^T P and dK^T += Q^T dS; X^T rows through the transposing
     // read: block bb of 16 lanes reads rows 16u + 4(bb/2) + {0..3} (+8),
     // columns 32 dt + 16 (bb%2) + {0..15}
@@ -311,31 +323,57 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
         dk_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qtr, as_f16x8(dsw[u]), dk_acc[dt], 0, 0, 0);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile st+1 has landed in LDS
-    if (st + 1 < n_steps) convert_own(buf ^ 1);
-    __syncthreads();
+    // this wave's copies for step i+1 have landed (each lane waits for its
+    // own; the wave's lanes run in lockstep, so the whole tile is there)
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   };
-  for (int st = 0; st < n_steps; st += 2) {
-    step(st, std::integral_constant<int, 0>{});
-    if (st + 1 < n_steps) step(st + 1, std::integral_constant<int, 1>{});
+  for (int i = 0; i < n_mine; i += 2) {
+    step(i, std::integral_constant<int, 0>{});
+    if (i + 1 < n_mine) step(i + 1, std::integral_constant<int, 1>{});
   }
 
-  // epilogue: lane holds key lane%32, d = 32 dt + 8 r4 + 4 half + 0..3
-  if (key_ok) {
-    uint16_t* kp = a.dk + ((size_t)(s0 + key) * Hkv + g) * D + 4 * half;
-    uint16_t* vp = a.dv + ((size_t)(s0 + key) * Hkv + g) * D + 4 * half;
-    const float sc = a.scale;
+  // sum the four waves' partials in wave order: wave w's dK^T / dV^T go to
+  // [key][d] fp32 in the tile arrays (dK: q_lds, dV: d_lds; waves 0-1 in
+  // buffer 0, 2-3 in buffer 1)
+  __syncthreads();
+  {
+    MIATTN_LDS float* kp = (MIATTN_LDS float*)(wave < 2 ? q_lds0 : q_lds1) + (wave & 1) * QT * D;
+    MIATTN_LDS float* vp = (MIATTN_LDS float*)(wave < 2 ? d_lds0 : d_lds1) + (wave & 1) * QT * D;
+    const int kr = lane & 31;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x16& K = dk_acc[dt];
-        const f32x16& V = dv_acc[dt];
-        u32x2 wk = {pack_bf16x2(K[4 * r4] * sc, K[4 * r4 + 1] * sc), pack_bf16x2(K[4 * r4 + 2] * sc, K[4 * r4 + 3] * sc)};
-        u32x2 wv = {pack_bf16x2(V[4 * r4], V[4 * r4 + 1]), pack_bf16x2(V[4 * r4 + 2], V[4 * r4 + 3])};
-        *reinterpret_cast<u32x2*>(kp + 32 * dt + 8 * r4) = wk;
-        *reinterpret_cast<u32x2*>(vp + 32 * dt + 8 * r4) = wv;
+        const int d0 = 32 * dt + 8 * r4 + 4 * half;
+        f32x4 wk = {dk_acc[dt][4 * r4], dk_acc[dt][4 * r4 + 1], dk_acc[dt][4 * r4 + 2], dk_acc[dt][4 * r4 + 3]};
+        f32x4 wv = {dv_acc[dt][4 * r4], dv_acc[dt][4 * r4 + 1], dv_acc[dt][4 * r4 + 2], dv_acc[dt][4 * r4 + 3]};
+        *reinterpret_cast<MIATTN_LDS f32x4*>(kp + kr * D + d0) = wk;
+        *reinterpret_cast<MIATTN_LDS f32x4*>(vp + kr * D + d0) = wv;
       }
+  }
+  __syncthreads();
+  const float sc = a.scale;
+  for (int idx = threadIdx.x; idx < QT * (D / 4); idx += 256) {
+    const int kr = idx / (D / 4);
+    const int d0 = 4 * (idx % (D / 4));
+    const int kk_ = kb0 + kr;
+    if (kk_ >= L) continue;
+    const int eo = kr * D + d0;
+    const f32x4 k0 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds0 + eo);
+    const f32x4 k1 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds0 + QT * D + eo);
+    const f32x4 k2 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds1 + eo);
+    const f32x4 k3 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds1 + QT * D + eo);
+    const f32x4 v0 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds0 + eo);
+    const f32x4 v1 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds0 + QT * D + eo);
+    const f32x4 v2 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds1 + eo);
+    const f32x4 v3 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds1 + QT * D + eo);
+    const f32x4 ks = (((k0 + k1) + k2) + k3) * sc;
+    const f32x4 vs = ((v0 + v1) + v2) + v3;
+    const size_t go = ((size_t)(s0 + kk_) * Hkv + g) * D + d0;
+    u32x2 wk = {pack_bf16x2(ks[0], ks[1]), pack_bf16x2(ks[2], ks[3])};
+    u32x2 wv = {pack_bf16x2(vs[0], vs[1]), pack_bf16x2(vs[2], vs[3])};
+    *reinterpret_cast<u32x2*>(a.dk + go) = wk;
+    *reinterpret_cast<u32x2*>(a.dv + go) = wv;
   }
 }
 
@@ -343,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
 // Workgroup = 4 waves over NH = min(G, 4) query heads of one kv head and 4/NH
 // blocks of 32 query rows; K/V tiles of 32 KB keys are shared by the waves.
 template <int D, int KB, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void miattn_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void miattn_bwd_dq_kernel(BwdArgs a) {
   using TL = BwdTile<D>;
   constexpr int CH = TL::CH;
   constexpr int BC = 32 * KB;
@@ -394,7 +432,8 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dq_kernel(BwdArgs a) {
   const int qrow = q0 + (lane & 31);
   const bool q_ok = qrow < L;
 
-  // Q and dO of this lane's query row as B operands; its LSE and Delta
+  // Q and dO of this lane's query row as B operands (fp16 copies); its LSE
+  // and Delta
   u32x4 qop[NKK], dop[NKK];
   float l2, dlt;
   {
@@ -402,17 +441,17 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const u32x4 z = {0u, 0u, 0u, 0u};
-      qop[kk] = q_ok ? bf16x8_to_f16x8(ld16(a.q + off + 16 * kk)) : z;
-      dop[kk] = q_ok ? bf16x8_to_f16x8(ld16(a.dout + off + 16 * kk)) : z;
+      qop[kk] = q_ok ? ld16(a.q16 + off + 16 * kk) : z;
+      dop[kk] = q_ok ? ld16(a.do16 + off + 16 * kk) : z;
     }
-    const size_t si = (size_t)h * a.total_tokens + s0 + (q_ok ? qrow : 0);
-    l2 = lse_to_log2(a.lse[si]);
-    dlt = a.delta[si];
+    const size_t si = (size_t)h * a.t_pad + s0 + (q_ok ? qrow : 0);
+    l2 = a.stats[si];
+    dlt = a.stats[(size_t)Hq * a.t_pad + si];
   }
 
   const size_t kv_row = (size_t)Hkv * D;
-  const uint16_t* kbase = a.k + (size_t)s0 * kv_row + (size_t)g * D;
-  const uint16_t* vbase = a.v + (size_t)s0 * kv_row + (size_t)g * D;
+  const uint16_t* kbase = a.k16 + (size_t)s0 * kv_row + (size_t)g * D;
+  const uint16_t* vbase = a.v16 + (size_t)s0 * kv_row + (size_t)g * D;
   uint32_t koff[NI];
 #pragma unroll
   for (int j = 0; j < NI; ++j) {
@@ -438,15 +477,6 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dq_kernel(BwdArgs a) {
       dma16_to_lds(vb0, off, vbuf(buf) + (wave * NI + j) * 1024);
     }
   };
-  auto convert_own = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < NI; ++j) {
-      MIATTN_LDS uint8_t* pk = kbuf(buf) + (wave * NI + j) * 1024 + 16 * lane;
-      MIATTN_LDS uint8_t* pv = vbuf(buf) + (wave * NI + j) * 1024 + 16 * lane;
-      lds_st16(pk, bf16x8_to_f16x8(lds_ld16(pk)));
-      lds_st16(pv, bf16x8_to_f16x8(lds_ld16(pv)));
-    }
-  };
 
   const int kend_wg = CAUSAL ? (qt * QR + QR < L ? qt * QR + QR : L) : L;
   const int n_kt = (kend_wg + BC - 1) / BC;
@@ -461,7 +491,6 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dq_kernel(BwdArgs a) {
 
   if (n_kt > 0) load_tile(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  if (n_kt > 0) convert_own(0);
   __syncthreads();
 
   auto step = [&](int kt, auto bufc) {
@@ -486,20 +515,21 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dq_kernel(BwdArgs a) {
           s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(lds_ld16(kl + so)), as_f16x8(qop[kk]), s, 0, 0, 0);
           dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(lds_ld16(vl + so)), as_f16x8(dop[kk]), dp, 0, 0, 0);
         }
-        // dS^T = P^T (dP^T - Delta), masked outside the sequence and above
-        // the diagonal
+        // dS^T = P^T (dP^T - Delta), 0 outside the sequence and above the
+        // diagonal
         u32x4 dsw[2];
 #pragma unroll
-        for (int i = 0; i < 16; i += 2) {
+        for (int e0 = 0; e0 < 16; e0 += 2) {
           float d[2];
 #pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int key = kt * BC + 32 * kb + 8 * ((i + e) >> 2) + 4 * half + ((i + e) & 3);
+          for (int u = 0; u < 2; ++u) {
+            const int e = e0 + u;
+            const int key = kt * BC + 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
             const bool ok = q_ok && key < L && (!CAUSAL || key <= qrow);
-            const float p = ok ? exp2_hw(__builtin_fmaf(s[i + e], c, -l2)) : 0.f;
-            d[e] = p * (dp[i + e] - dlt);
+            const float p = exp2_hw(__builtin_fmaf(s[e], c, -l2));
+            d[u] = ok ? p * (dp[e] - dlt) : 0.f;
           }
-          dsw[i >> 3][(i >> 1) & 3] = pack_f16x2(d[0], d[1]);
+          dsw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(d[0], d[1]);
         }
         // dQ^T += K^T dS^T; K^T rows (keys) through the transposing read
 #pragma unroll
@@ -518,7 +548,6 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dq_kernel(BwdArgs a) {
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if (kt + 1 < n_kt) convert_own(buf ^ 1);
     __syncthreads();
   };
   for (int kt = 0; kt < n_kt; kt += 2) {

@@ -463,10 +463,17 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
   return ok();
 }
 
-size_t miattn_attn_bwd_workspace_bytes(int total_tokens, int num_q_heads) {
-  if (total_tokens <= 0 || num_q_heads <= 0) return 0;
-  const size_t bytes = (size_t)total_tokens * num_q_heads * sizeof(float);
-  return (bytes + 255) & ~(size_t)255;
+namespace {
+// row length of the backward's stats arrays: T plus a 32-row tile of slack,
+// rounded up to 64
+long bwd_t_pad(int total_tokens) { return ((long)total_tokens + 32 + 63) / 64 * 64; }
+}  // namespace
+
+size_t miattn_attn_bwd_workspace_bytes(int total_tokens, int num_q_heads, int num_kv_heads, int head_dim) {
+  if (total_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+  const size_t stats = 2 * (size_t)num_q_heads * bwd_t_pad(total_tokens) * sizeof(float);
+  const size_t copies = 2 * (size_t)total_tokens * (num_q_heads + num_kv_heads) * head_dim * 2;
+  return ((stats + 255) & ~(size_t)255) + ((copies + 255) & ~(size_t)255);
 }
 
 int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout, const float* lse,
@@ -487,9 +494,10 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
   const int G = num_q_heads / num_kv_heads;
   if (!(G == 1 || G == 2 || G % 4 == 0))
     return fail(MIATTN_ERR_UNSUPPORTED, "%s: Hq/Hkv must be 1, 2 or a multiple of 4", who);
-  if ((long)total_tokens * num_q_heads * head_dim > 0x7fffffffL)
+  if ((long)total_tokens * num_q_heads * head_dim > 0x7fffffffL ||
+      2L * num_q_heads * bwd_t_pad(total_tokens) > 0x3fffffffL)
     return fail(MIATTN_ERR_INVALID_ARG, "%s: tensors above 2^31 elements are not supported", who);
-  const size_t need = miattn_attn_bwd_workspace_bytes(total_tokens, num_q_heads);
+  const size_t need = miattn_attn_bwd_workspace_bytes(total_tokens, num_q_heads, num_kv_heads, head_dim);
   if (workspace != nullptr && workspace_bytes < need)
     return fail(MIATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", who, workspace_bytes, need);
   const int dev = current_device();
@@ -500,25 +508,34 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
     const int r = library_workspace(dev, need, &ws, who);
     if (r) return r;
   }
+  const long t_pad = bwd_t_pad(total_tokens);
+  const size_t stats_bytes = (2 * (size_t)num_q_heads * t_pad * sizeof(float) + 255) & ~(size_t)255;
+  const size_t nq = (size_t)total_tokens * num_q_heads * head_dim;
+  const size_t nk = (size_t)total_tokens * num_kv_heads * head_dim;
   miattn::BwdArgs a{};
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
-  a.o = (const uint16_t*)o; a.dout = (const uint16_t*)dout; a.lse = lse; a.delta = (float*)ws;
+  a.o = (const uint16_t*)o; a.dout = (const uint16_t*)dout; a.lse = lse;
+  a.stats = (float*)ws;
+  a.q16 = (uint16_t*)((char*)ws + stats_bytes);
+  a.do16 = a.q16 + nq;
+  a.k16 = a.do16 + nq;
+  a.v16 = a.k16 + nk;
   a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
-  a.cu_seqlens = cu_seqlens; a.num_seqs = num_seqs; a.total_tokens = total_tokens;
+  a.cu_seqlens = cu_seqlens; a.num_seqs = num_seqs; a.total_tokens = total_tokens; a.t_pad = (int)t_pad;
   a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
   a.heads_per_wg = G >= 4 ? 4 : G;
   a.n_head_slots = num_kv_heads * (G / a.heads_per_wg);
   a.c = scale * miattn::kLog2e;
   a.scale = scale;
-  const long rows = (long)total_tokens * num_q_heads;
+  const long rows = (long)total_tokens * (num_q_heads + num_kv_heads);
   const int rpb = 256 / (head_dim / 8);
-  const unsigned g_delta = (unsigned)((rows + rpb - 1) / rpb);
-  const unsigned g_dkdv = (unsigned)((long)num_kv_heads * ((max_seqlen + 127) / 128) * num_seqs);
+  const unsigned g_prep = (unsigned)((rows + rpb - 1) / rpb);
+  const unsigned g_dkdv = (unsigned)((long)num_kv_heads * ((max_seqlen + 31) / 32) * num_seqs);
   const int QR = 32 * (4 / a.heads_per_wg);
   const unsigned g_dq = (unsigned)((long)a.n_head_slots * ((max_seqlen + QR - 1) / QR) * num_seqs);
   const dim3 blk(256);
   if (head_dim == 64) {
-    hipLaunchKernelGGL(miattn::miattn_bwd_delta_kernel<64>, dim3(g_delta), blk, 0, st, a);
+    hipLaunchKernelGGL(miattn::miattn_bwd_prep_kernel<64>, dim3(g_prep), blk, 0, st, a);
     if (causal) {
       hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<64, true>), dim3(g_dkdv), blk, 0, st, a);
       hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<64, 2, true>), dim3(g_dq), blk, 0, st, a);
@@ -527,7 +544,7 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
       hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<64, 2, false>), dim3(g_dq), blk, 0, st, a);
     }
   } else {
-    hipLaunchKernelGGL(miattn::miattn_bwd_delta_kernel<128>, dim3(g_delta), blk, 0, st, a);
+    hipLaunchKernelGGL(miattn::miattn_bwd_prep_kernel<128>, dim3(g_prep), blk, 0, st, a);
     if (causal) {
       hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<128, true>), dim3(g_dkdv), blk, 0, st, a);
       hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<128, 2, true>), dim3(g_dq), blk, 0, st, a);

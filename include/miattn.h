@@ -260,8 +260,11 @@ size_t miattn_decode_numerics_workspace_bytes(int batch, int num_q_heads, int he
  *   dq [total_tokens, Hq, D], dk, dv [total_tokens, Hkv, D] bf16 (written).
  *   head_dim 64 or 128; Hq/Hkv 1, 2 or a multiple of 4 (MIATTN_ERR_UNSUPPORTED
  *   otherwise).
- *   workspace: miattn_attn_bwd_workspace_bytes bytes of device scratch (the
- *   fp32 row sums of dO o O), or NULL for the library-owned buffer.
+ *   workspace: miattn_attn_bwd_workspace_bytes bytes of device scratch (row
+ *   terms and fp16 copies of the inputs), or NULL for the library-owned
+ *   buffer. Inputs must lie inside fp16's range (|x| <= 65504): the products
+ *   run on fp16 operands, to which bf16 values inside that range convert
+ *   exactly.
  * Deterministic: fixed reduction orders, no atomics; dQ is computed by its own
  * pass over the keys rather than accumulated across workgroups.
  */
@@ -271,9 +274,11 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
                     int causal, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                     void* stream);
 
-/* Bytes of workspace miattn_attn_bwd needs: total_tokens * Hq floats,
- * rounded up to 256 (0 for an empty problem). */
-size_t miattn_attn_bwd_workspace_bytes(int total_tokens, int num_q_heads);
+/* Bytes of workspace miattn_attn_bwd needs: the fp32 row terms and log2-unit
+ * LSE (2 * Hq * (total_tokens + 32..95) floats) and fp16 copies of q, dout, k
+ * and v (2 * total_tokens * (Hq + Hkv) * head_dim halves), each rounded up to
+ * 256 bytes; 0 for an empty problem. */
+size_t miattn_attn_bwd_workspace_bytes(int total_tokens, int num_q_heads, int num_kv_heads, int head_dim);
 
 /* Split count chosen for num_splits == 0: the candidate set and efficiency of
  * miattn_split_heuristic with this library's MI355X capacity (256 compute

@@ -310,5 +310,6 @@ def test_bwd_validation(kw, code):
 def test_bwd_empty_is_noop_and_workspace_size():
     assert _bwd(n=0, q=None) == mi.OK
     assert _bwd(T=0, q=None) == mi.OK
-    assert mi.attn_bwd_workspace_bytes(100, 3) == 1280
-    assert mi.attn_bwd_workspace_bytes(0, 3) == 0
+    # stats: 2 x 3 heads x 192 padded rows x 4 B = 4608; copies 2 x 100 x 4 x 64 x 2 = 102400
+    assert mi.attn_bwd_workspace_bytes(100, 3, 1, 64) == 4608 + 102400
+    assert mi.attn_bwd_workspace_bytes(0, 3, 1, 64) == 0
