@@ -67,3 +67,20 @@ def chunked_prefill_bytes(q_lens, k_lens, num_q_heads: int, num_kv_heads: int, h
     lse = tq * num_q_heads * 4 if with_lse else 0
     bt = sum((int(x) + page_size - 1) // page_size for x in k_lens) * 4
     return float(qo + kv + lse + bt)
+
+
+def backward_flops(seqlens, num_q_heads: int, head_dim: int, causal: bool) -> float:
+    """Backward by recomputation: five products per admissible pair (S = Q K^T,
+    dP = dO V^T, dV += P^T dO, dK += dS^T Q, dQ += dS K), 2 D flops each, i.e.
+    2.5 times the forward's count. Recomputing S and dP a second time for dQ
+    (as a deterministic implementation without atomics may) is not credited."""
+    return 2.5 * prefill_flops(seqlens, num_q_heads, head_dim, causal)
+
+
+def backward_bytes(total_tokens: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                   elem_bytes: int = 2) -> float:
+    """Bytes the backward must move once: Q, O, dO read and dQ written per
+    query head; K, V read and dK, dV written per kv head; the LSE read."""
+    q_side = 4 * total_tokens * num_q_heads * head_dim * elem_bytes
+    kv_side = 4 * total_tokens * num_kv_heads * head_dim * elem_bytes
+    return float(q_side + kv_side + total_tokens * num_q_heads * 4)

@@ -90,6 +90,21 @@ __device__ __forceinline__ float lse_to_log2(float lse) {
   return lse == kNegInf ? __builtin_inff() : lse * kLog2e;
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Direct HBM -> LDS copy of 16 bytes per lane (buffer load, LDS form) issued
+// from inline asm: lane i's 16 bytes from base + voff land at LDS byte
+// address lds + 16 i. The compiler does not track these writes, so a loop
+// that reads one LDS buffer while a copy fills the other needs no waits from
+// it; the caller waits (s_waitcnt vmcnt) before reading what was copied.
+// base and lds must be uniform.
+__device__ __forceinline__ void dma16_to_lds_asm(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t addr = (uint64_t)base;
+  const i32x4 rs = {(int)(uint32_t)addr, (int)((addr >> 32) & 0xffff), 0x7fffffff, 0x00020000};
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs) : "memory");
+}
+
 // ---------------------------------------------------------------- prep
 // Rows (token, query head) give Delta = dO . O in fp32, the LSE in log2 units
 // and fp16 copies of Q and dO; rows (token, kv head) give fp16 copies of K and
@@ -153,6 +168,7 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t d_lds1[4 * TILE];
   __shared__ __attribute__((aligned(16))) float st_lds0[4 * 64];   // per wave: 32 LSE, 32 Delta
   __shared__ __attribute__((aligned(16))) float st_lds1[4 * 64];
+  __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[2 * TILE];   // the 32 keys' K, then V
 
   // work item: (kv head, key block, sequence), kv head fastest; key block 0
   // (the most causal work) first
@@ -178,22 +194,36 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
   const int key = kb0 + (lane & 31);                 // this lane's key column
   const bool key_ok = key < L;
 
-  MIATTN_LDS uint8_t* qb[2] = {(MIATTN_LDS uint8_t*)q_lds0 + wave * TILE, (MIATTN_LDS uint8_t*)q_lds1 + wave * TILE};
-  MIATTN_LDS uint8_t* db[2] = {(MIATTN_LDS uint8_t*)d_lds0 + wave * TILE, (MIATTN_LDS uint8_t*)d_lds1 + wave * TILE};
-  MIATTN_LDS float* sb[2] = {(MIATTN_LDS float*)st_lds0 + wave * 64, (MIATTN_LDS float*)st_lds1 + wave * 64};
+  // this wave's buffers: LDS byte addresses (the copies are issued from asm)
+  const uint32_t qaddr0 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)q_lds0 + wave * TILE);
+  const uint32_t qaddr1 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)q_lds1 + wave * TILE);
+  const uint32_t daddr0 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)d_lds0 + wave * TILE);
+  const uint32_t daddr1 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)d_lds1 + wave * TILE);
+  const uint32_t saddr0 = (uint32_t)(uintptr_t)((MIATTN_LDS float*)st_lds0 + wave * 64);
+  const uint32_t saddr1 = (uint32_t)(uintptr_t)((MIATTN_LDS float*)st_lds1 + wave * 64);
 
-  // K, V of the 32 keys as B operands: lane holds key lane%32,
-  // d = 16 kk + 8 half + 0..7 (fp16 copies)
-  u32x4 kop[NKK], vop[NKK];
+  // K, V of the 32 keys (fp16 copies) in LDS, swizzled like the Q/dO tiles,
+  // read as B operands (lane: key lane%32, d = 16 kk + 8 half + 0..7) at the
+  // same offsets as the Q/dO operand reads; keys past the sequence end
+  // repeat its last key (their P and dS are masked to 0). Each wave copies
+  // NC/4 of the 1-KB pieces of each.
   {
-    const size_t off = ((size_t)(s0 + (key_ok ? key : 0)) * Hkv + g) * D + 8 * half;
+    const size_t kv_row = (size_t)Hkv * D;
+    const char* ksrc = (const char*)(a.k16 + (size_t)(s0 + kb0) * kv_row + (size_t)g * D);
+    const char* vsrc = (const char*)(a.v16 + (size_t)(s0 + kb0) * kv_row + (size_t)g * D);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      kop[kk] = key_ok ? ld16(a.k16 + off + 16 * kk) : z;
-      vop[kk] = key_ok ? ld16(a.v16 + off + 16 * kk) : z;
+    for (int j = wave; j < NC; j += 4) {
+      const int lidx = j * 64 + lane;
+      const int r = lidx / CH;
+      const int slot = lidx % CH;
+      const int rr = kb0 + r < L ? r : L - 1 - kb0;
+      const uint32_t off = (uint32_t)(((size_t)rr * kv_row + 8 * (slot ^ TL::swz(r))) * 2);
+      dma16_to_lds(ksrc, off, (MIATTN_LDS uint8_t*)kv_lds + j * 1024);
+      dma16_to_lds(vsrc, off, (MIATTN_LDS uint8_t*)kv_lds + TILE + j * 1024);
     }
   }
+  const MIATTN_LDS uint8_t* k_l = (const MIATTN_LDS uint8_t*)kv_lds;
+  const MIATTN_LDS uint8_t* v_l = (const MIATTN_LDS uint8_t*)kv_lds + TILE;
 
   // steps: (query head of the group, query tile); causal tiles start at the
   // one holding query kb0; this wave takes steps wave, wave + 4, ...
@@ -233,11 +263,11 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
         const int rr = q0 + r < L ? r : L - 1 - q0;
         off -= (uint32_t)((size_t)(r - rr) * q_row * 2);
       }
-      dma16_to_lds(qsrc, off, qb[buf] + j * 1024);
-      dma16_to_lds(dsrc, off, db[buf] + j * 1024);
+      dma16_to_lds_asm(qsrc, off, (buf ? qaddr1 : qaddr0) + j * 1024);
+      dma16_to_lds_asm(dsrc, off, (buf ? daddr1 : daddr0) + j * 1024);
     }
     if (lane < 16)
-      dma16_to_lds(a.stats, st_lane + (uint32_t)(((size_t)h * a.t_pad + s0 + q0) * 4), sb[buf]);
+      dma16_to_lds_asm(a.stats, st_lane + (uint32_t)(((size_t)h * a.t_pad + s0 + q0) * 4), buf ? saddr1 : saddr0);
   };
 
   f32x16 dk_acc[NDT], dv_acc[NDT];
@@ -251,20 +281,24 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
 
   if (n_mine > 0) load_tile(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();   // the K/V block copied by all four waves
 
-  auto step = [&](int i, auto bufc) {
-    constexpr int buf = decltype(bufc)::value;
+  // one loop body for both buffers (a copy per buffer would give the
+  // accumulators a different register home in each and copies between them)
+  for (int i = 0; i < n_mine; ++i) {
+    const int buf = i & 1;
     if (i + 1 < n_mine) load_tile(i + 1, buf ^ 1);
-    const MIATTN_LDS uint8_t* ql = qb[buf];
-    const MIATTN_LDS uint8_t* dl_ = db[buf];
+    const MIATTN_LDS uint8_t* ql = (const MIATTN_LDS uint8_t*)(uintptr_t)(buf ? qaddr1 : qaddr0);
+    const MIATTN_LDS uint8_t* dl_ = (const MIATTN_LDS uint8_t*)(uintptr_t)(buf ? daddr1 : daddr0);
+    const MIATTN_LDS float* sl = (const MIATTN_LDS float*)(uintptr_t)(buf ? saddr1 : saddr0);
     const int st = wave + 4 * i;
     const int q0 = (qt0 + st % nq) * QT;
     // this lane's 16 rows: 8 (e/4) + 4 half + e%4
     float l2[16], dl[16];
 #pragma unroll
     for (int gi = 0; gi < 4; ++gi) {
-      const f32x4 lv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sb[buf] + 8 * gi + 4 * half);
-      const f32x4 dv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sb[buf] + 32 + 8 * gi + 4 * half);
+      const f32x4 lv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sl + 8 * gi + 4 * half);
+      const f32x4 dv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sl + 32 + 8 * gi + 4 * half);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         l2[4 * gi + e] = lv[e];
@@ -279,30 +313,49 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
       dp[r] = 0.f;
     }
     {
+      // operands of step kk + 1 are read while step kk's products issue
       const int r = lane & 31;
+      auto so = [&](int kk) { return r * (2 * D) + 16 * ((2 * kk + half) ^ TL::swz(r)); };
+      u32x4 oq = lds_ld16(ql + so(0)), ok_ = lds_ld16(k_l + so(0));
+      u32x4 od = lds_ld16(dl_ + so(0)), ov = lds_ld16(v_l + so(0));
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        const int so = r * (2 * D) + 16 * ((2 * kk + half) ^ TL::swz(r));
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(lds_ld16(ql + so)), as_f16x8(kop[kk]), s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(lds_ld16(dl_ + so)), as_f16x8(vop[kk]), dp, 0, 0, 0);
+        u32x4 nq = oq, nk = ok_, nd = od, nv = ov;
+        if (kk + 1 < NKK) {
+          nq = lds_ld16(ql + so(kk + 1));
+          nk = lds_ld16(k_l + so(kk + 1));
+          nd = lds_ld16(dl_ + so(kk + 1));
+          nv = lds_ld16(v_l + so(kk + 1));
+        }
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(oq), as_f16x8(ok_), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(od), as_f16x8(ov), dp, 0, 0, 0);
+        oq = nq; ok_ = nk; od = nd; ov = nv;
       }
     }
     // P = exp2(s c - lse2) and dS = P (dP - Delta), both 0 outside the
-    // sequence and (causal) above the diagonal
+    // sequence and (causal) above the diagonal; only tail and diagonal
+    // tiles need the mask (uniform test)
+    const bool need_mask = kb0 + 32 > L || q0 + QT > L || (CAUSAL && kb0 + 31 > q0);
+    float p[16], d[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = exp2_hw(__builtin_fmaf(s[e], c, -l2[e]));
+      d[e] = p[e] * (dp[e] - dl[e]);
+    }
+    if (need_mask) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int qrow = q0 + 8 * (e >> 2) + 4 * half + (e & 3);
+        const bool ok = key_ok & (qrow < L) & (!CAUSAL | (key <= qrow));
+        p[e] = ok ? p[e] : 0.f;
+        d[e] = ok ? d[e] : 0.f;
+      }
+    }
     u32x4 pw[2], dsw[2];
 #pragma unroll
     for (int e0 = 0; e0 < 16; e0 += 2) {
-      float p[2], d[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int e = e0 + u;
-        const int qrow = q0 + 8 * (e >> 2) + 4 * half + (e & 3);
-        const bool ok = key_ok && qrow < L && (!CAUSAL || key <= qrow);
-        p[u] = ok ? exp2_hw(__builtin_fmaf(s[e], c, -l2[e])) : 0.f;
-        d[u] = ok ? p[u] * (dp[e] - dl[e]) : 0.f;
-      }
-      pw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(p[0], p[1]);
-      dsw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(d[0], d[1]);
+      pw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(p[e0], p[e0 + 1]);
+      dsw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(d[e0], d[e0 + 1]);
     }
     // dV^T += dO^T P and dK^T += Q^T dS; X^T rows through the transposing
     // read: block bb of 16 lanes reads rows 16u + 4(bb/2) + {0..3} (+8),
@@ -326,10 +379,6 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
     // this wave's copies for step i+1 have landed (each lane waits for its
     // own; the wave's lanes run in lockstep, so the whole tile is there)
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  };
-  for (int i = 0; i < n_mine; i += 2) {
-    step(i, std::integral_constant<int, 0>{});
-    if (i + 1 < n_mine) step(i + 1, std::integral_constant<int, 1>{});
   }
 
   // sum the four waves' partials in wave order: wave w's dK^T / dV^T go to

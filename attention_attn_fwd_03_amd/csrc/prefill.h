@@ -118,8 +118,10 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
   const int lin = blockIdx.x;
   const int hslot = lin % a.n_head_slots;
   const int rest = lin / a.n_head_slots;
-  const int pair = rest / a.num_seqs;
-  const int b = rest % a.num_seqs;
+  // paged (chunked prefill): a sequence's tiles are consecutive, so the
+  // workgroups running together on an XCD share one prefix in its L2
+  const int pair = PAGED ? rest % a.n_pairs : rest / a.num_seqs;
+  const int b = PAGED ? rest / a.n_pairs : rest % a.num_seqs;
   int s0 = a.cu_seqlens[b];
   int s1 = a.cu_seqlens[b + 1];
   s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);

@@ -205,6 +205,8 @@ TRAFFIC_KERNELS = {
     "decode_paged_b64": ("decode", ["miattn_decode_split_kernel", "miattn_combine_kernel"]),
     "decode_long_ctx131072": ("long", ["miattn_decode_split_kernel", "miattn_combine_kernel"]),
     "chunked_prefill_8x1024": ("chunked", ["miattn_prefill_fwd_kernel"]),
+    "backward_causal_gqa_s4096": ("backward", ["miattn_bwd_prep_kernel", "miattn_bwd_dkdv_kernel",
+                                               "miattn_bwd_dq_kernel"]),
 }
 
 
@@ -273,7 +275,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = library policy")
     ap.add_argument("--long-splits", type=int, default=0, help="0 = library policy")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "chunked", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "chunked", "backward", "copy"], default=None,
                     help="profiling aid: run just one stage (or a 1 GiB device copy used to calibrate "
                          "the HBM byte counters) for --steps iterations and print its mean time")
     ap.add_argument("--sweep-splits", action="store_true",
@@ -330,13 +332,22 @@ def main():
         return
 
     print("[bench] generating inputs", file=sys.stderr, flush=True)
-    want = {"prefill", "decode", "long", "chunked"} if args.only is None else {args.only}
+    want = {"prefill", "decode", "long", "chunked", "backward"} if args.only is None else {args.only}
     P = Dd = Ld = None
     pc = synth.config2(S=4096, seed=0)
-    if "prefill" in want:
+    if "prefill" in want or "backward" in want:
         P = dict(q=bf16(pc.q), k=bf16(pc.k), v=bf16(pc.v), cu=i32(pc.cu_seqlens))
         P["o"] = torch.empty_like(P["q"])
         P["lse"] = torch.empty((pc.num_q_heads, pc.total_tokens), dtype=torch.float32, device=dev)
+    if "backward" in want:
+        # the same causal GQA problem: forward outputs once, then the backward
+        # on a seeded upstream gradient
+        mi.attn_fwd(P["q"], P["k"], P["v"], P["cu"], pc.max_seqlen, scale=pc.scale, causal=True,
+                    out=P["o"], lse=P["lse"])
+        P["do"] = bf16(synth.output_gradient(9, 0, pc.total_tokens, pc.num_q_heads, pc.head_dim))
+        P["dq"] = torch.empty_like(P["q"])
+        P["dk"] = torch.empty_like(P["k"])
+        P["dv"] = torch.empty_like(P["v"])
     dc = synth.config3(seed=0, tail="zero") if "decode" in want else None
     if dc is not None:
         Dd = dict(q=bf16(dc.q), kc=bf16(dc.k_cache), vc=bf16(dc.v_cache), bt=i32(dc.block_table),
@@ -363,6 +374,10 @@ def main():
         mi.attn_fwd_paged(Cd["q"], Cd["kc"], Cd["vc"], Cd["bt"], Cd["cu"], Cd["sk"], cc.max_seqlen_q,
                           scale=cc.scale, causal=True, out=Cd["o"], lse=Cd["lse"])
 
+    def backward():
+        mi.attn_bwd(P["q"], P["k"], P["v"], P["o"], P["lse"], P["do"], P["cu"], pc.max_seqlen, scale=pc.scale,
+                    causal=True, dq=P["dq"], dk=P["dk"], dv=P["dv"])
+
     def prefill():
         mi.attn_fwd(P["q"], P["k"], P["v"], P["cu"], pc.max_seqlen, scale=pc.scale, causal=True,
                     out=P["o"], lse=P["lse"])
@@ -377,7 +392,8 @@ def main():
 
     stages = [prefill, decode, long_decode]
     if args.only is not None:
-        f = {"prefill": prefill, "decode": decode, "long": long_decode, "chunked": chunked}[args.only]
+        f = {"prefill": prefill, "decode": decode, "long": long_decode, "chunked": chunked,
+             "backward": backward}[args.only]
         for _ in range(args.warmup):
             f()
         torch.cuda.synchronize()
@@ -423,6 +439,20 @@ def main():
     ce1.record(stream)
     torch.cuda.synchronize()
     t_chunk = ce0.elapsed_time(ce1) / args.steps * 1e-3
+    # backward of the prefill workload (beside the step as well)
+    for _ in range(args.warmup):
+        backward()
+    be0 = torch.cuda.Event(enable_timing=True)
+    be1 = torch.cuda.Event(enable_timing=True)
+    be0.record(stream)
+    for _ in range(args.steps):
+        backward()
+    be1.record(stream)
+    torch.cuda.synchronize()
+    t_bwd = be0.elapsed_time(be1) / args.steps * 1e-3
+    fl_bwd = accounting.backward_flops(pc.seqlens, pc.num_q_heads, pc.head_dim, True)
+    by_bwd = accounting.backward_bytes(pc.total_tokens, pc.num_q_heads, pc.num_kv_heads, pc.head_dim)
+
     fl_chunk = accounting.chunked_prefill_flops(cc.q_lens, cc.seq_lens_k, cc.num_q_heads, cc.head_dim, True)
     by_chunk = accounting.chunked_prefill_bytes(cc.q_lens, cc.seq_lens_k, cc.num_q_heads, cc.num_kv_heads,
                                                 cc.head_dim)
@@ -451,7 +481,8 @@ def main():
         "config": {
             "workload": "causal GQA prefill Hq=32 Hkv=8 D=128 S=4096 + paged decode B=64 ctx U[512,4096] "
                         "shuffled 16-token pages + long decode B=1 Hq=16 Hkv=4 D=256 ctx=131072 (one step); "
-                        "chunked prefill 8 chunks x 1024 after prefixes U[0,6144] reported beside it",
+                        "chunked prefill 8 chunks x 1024 after prefixes U[0,6144] and the prefill's backward "
+                        "reported beside it",
             "prefill": {"S": 4096, "Hq": 32, "Hkv": 8, "D": 128, "causal": True, "ms": round(t_pre * 1e3, 4),
                         "algorithmic_gflop": round(fl_pre / 1e9, 3)},
             "decode_paged": {"B": dc.batch, "tokens": int(dc.seq_lens.sum()), "splits": dsplits,
@@ -470,6 +501,14 @@ def main():
                                 "algorithmic_MB": round(by_chunk / 1e6, 2),
                                 "traffic": traffic_from_profile("chunked_prefill_8x1024", by_chunk),
                                 "timing": "its own loop of --steps calls after the step loop"},
+            "backward": {"S": 4096, "Hq": 32, "Hkv": 8, "D": 128, "causal": True, "ms": round(t_bwd * 1e3, 4),
+                         "TFLOP/s": round(fl_bwd / t_bwd / 1e12, 2),
+                         "frac_mfma": round(fl_bwd / t_bwd / 1e12 / PEAK_BF16_TFLOPS, 4),
+                         "algorithmic_gflop": round(fl_bwd / 1e9, 3),
+                         "algorithmic_MB": round(by_bwd / 1e6, 2),
+                         "traffic": traffic_from_profile("backward_causal_gqa_s4096", by_bwd),
+                         "work": "5 products per admissible pair (2.5x the forward)",
+                         "timing": "its own loop of --steps calls after the step loop"},
             "wall_s": round(wall, 4),
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
