@@ -343,6 +343,7 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
       d[e] = p[e] * (dp[e] - dl[e]);
     }
     if (need_mask) {
+      asm volatile("" ::: "memory");   // keep this a branch: the common tile skips it
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int qrow = q0 + 8 * (e >> 2) + 4 * half + (e & 3);

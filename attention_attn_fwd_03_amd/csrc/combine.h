@@ -3,12 +3,14 @@
 // FlashAttention 2 entry: fp32 normalised partial outputs weighted by
 // exp(LSE_s - max LSE)).
 //
-// Each workgroup owns one output row and up to 128 of its columns; each
-// thread owns four consecutive columns and a residue class of splits. Partial
-// sums are folded through LDS in a fixed order, so the result does not depend
-// on scheduling. Empty splits (LSE = -inf) are skipped; an all-empty row gives
+// Each workgroup owns one output row and up to 4 * cols of its columns (cols
+// float4 columns, chosen by the host so that even a few rows give enough
+// workgroups); each thread owns four consecutive columns and a residue class
+// of splits. Partial sums are folded through LDS in a fixed order, so the
+// result does not depend on scheduling. Empty splits (LSE = -inf) are skipped; an all-empty row gives
 // O = 0 and LSE = -inf.
 #pragma once
+#include "balance.h"
 #include "common.h"
 
 namespace miattn {
@@ -22,82 +24,159 @@ struct CombineArgs {
   int num_splits;
   int head_dim;
   int out_bf16;
+  int cols;               // float4 columns per workgroup (4 .. 32, power of two)
+  // decode partials in balanced groups (balance.h): row = b * Hq + h reads
+  // groups start_b .. start_b + s_b - 1 at [group][Hq][D]; seq_lens == null:
+  // the [rows][num_splits][D] layout
+  const int32_t* seq_lens;
+  int batch;
+  int max_pages;
+  int balance_units;
+  int num_q_heads;
 };
 
+// Block-wide max or sum of one float per thread (256 threads): a butterfly
+// inside each wave (every lane ends with the same value: each step adds the
+// same two numbers in every lane), then the four wave results in wave order.
 __device__ __forceinline__ float block_reduce(float v, float* red, bool is_max) {
-  const int t = threadIdx.x;
-  red[t] = v;
-  __syncthreads();
 #pragma unroll
-  for (int s = 128; s > 0; s >>= 1) {
-    if (t < s) red[t] = is_max ? fmaxf(red[t], red[t + s]) : red[t] + red[t + s];
-    __syncthreads();
+  for (int m = 32; m > 0; m >>= 1) {
+    const float o = __shfl_xor(v, m);
+    v = is_max ? fmaxf(v, o) : v + o;
   }
-  const float r = red[0];
+  __syncthreads();   // red may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
   __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < 4; ++i) r = is_max ? fmaxf(r, red[i]) : r + red[i];
   return r;
 }
 
-constexpr int kCombineCols = 32;   // float4 columns per workgroup (128 output columns)
+constexpr int kCombineCols = 32;   // most float4 columns per workgroup (128 output columns)
 constexpr int kCombineUnroll = 8;  // independent partial loads in flight per thread
 
-// Grid: (rows, ceil(D / 128)). Threads: kCombineCols column lanes x NG split
-// groups; group g sums splits g, g + NG, ... in increasing order.
+// Float4 columns per combine workgroup: 32 unless that leaves fewer than 512
+// workgroups (two per compute unit), then halved down to 4 (64 split groups).
+inline int combine_cols(long rows, int head_dim) {
+  const int dq = head_dim / 4;
+  int cols = kCombineCols;
+  while (cols > 4 && rows * ((dq + cols - 1) / cols) < 512) cols >>= 1;
+  return cols;
+}
+
+// Grid: (rows, ceil(D / (4 cols))). Threads: cols column lanes x NG = 256 /
+// cols split groups; group g sums splits g, g + NG, ... in increasing order.
 __global__ __launch_bounds__(256) void miattn_combine_kernel(CombineArgs a) {
-  __shared__ float red[256];
+  __shared__ float red[4];
   __shared__ f32x4 part[256];
+  __shared__ float wpart[256];
   const int row = blockIdx.x;
   const int S = a.num_splits;
   const int D = a.head_dim;
   const int DQ = D / 4;
-  const int col0 = blockIdx.y * kCombineCols;
-  const int ncol = DQ - col0 < kCombineCols ? DQ - col0 : kCombineCols;
+  const int col0 = blockIdx.y * a.cols;
+  const int ncol = DQ - col0 < a.cols ? DQ - col0 : a.cols;
   const int NG = 256 / ncol;
   const int t = threadIdx.x;
-  const float* pl = a.part_lse + (size_t)row * S;
-  const float* po = a.part_o + (size_t)row * S * D;
-
-  float mx = kNegInf;
-  for (int s = t; s < S; s += 256) mx = fmaxf(mx, pl[s]);
-  const float M = block_reduce(mx, red, true);
-  const bool empty = (M == kNegInf);
-  float ws = 0.f;
-  if (!empty)
-    for (int s = t; s < S; s += 256) {
-      const float x = pl[s];
-      ws += (x == kNegInf) ? 0.f : exp2_hw((x - M) * kLog2e);
-    }
-  const float W = block_reduce(ws, red, false);
-
   const int c = col0 + t % ncol;
   const int gi = t / ncol;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  if (!empty && gi < NG) {
-    for (int s0 = gi; s0 < S; s0 += NG * kCombineUnroll) {
-      f32x4 v[kCombineUnroll];
-      float x[kCombineUnroll];
+  // this row's partials: S of them, LSE s at pl[s * ls], output s at po + s * os
+  int S_row = S;
+  const float* pl = a.part_lse + (size_t)row * S;
+  const float* po = a.part_o + (size_t)row * S * D;
+  size_t ls = 1, os = D;
+  if (a.seq_lens != nullptr) {
+    const int Hq = a.num_q_heads;
+    const SplitPlan p = balanced_plan(a.seq_lens, a.batch, a.max_pages, a.balance_units, row / Hq, false);
+    S_row = p.count;
+    const size_t first = (size_t)p.start * Hq + row % Hq;
+    pl = a.part_lse + first;
+    po = a.part_o + first * D;
+    ls = Hq;
+    os = (size_t)Hq * D;
+  }
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+
+  float M, W;
+  f32x4 acc = z;
+  if (S_row <= NG * kCombineUnroll) {
+    // Every thread's splits (gi, gi + NG, ...) fit one batch: their loads are
+    // issued before the max is known; the weight sums travel with the
+    // partial sums through the fold below.
+    f32x4 v[kCombineUnroll];
+    float x[kCombineUnroll];
+    float mx = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kCombineUnroll; ++u) {
+      const int s = gi + u * NG;
+      const bool ok = gi < NG && s < S_row;
+      x[u] = ok ? pl[(size_t)s * ls] : kNegInf;
+      v[u] = ok ? *reinterpret_cast<const f32x4*>(po + (size_t)s * os + 4 * c) : z;
+      mx = fmaxf(mx, x[u]);
+    }
+    M = block_reduce(mx, red, true);
+    float ws = 0.f;
+    if (M != kNegInf) {
 #pragma unroll
       for (int u = 0; u < kCombineUnroll; ++u) {
-        const int s = s0 + u * NG;
-        const int sc = s < S ? s : S - 1;
-        x[u] = s < S ? pl[sc] : kNegInf;
-        v[u] = *reinterpret_cast<const f32x4*>(po + (size_t)sc * D + 4 * c);
-      }
-#pragma unroll
-      for (int u = 0; u < kCombineUnroll; ++u) {
-        const float w = exp2_hw((x[u] - M) * kLog2e);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        acc += (x[u] == kNegInf) ? z : w * v[u];
+        const bool skip = x[u] == kNegInf;
+        const float w = skip ? 0.f : exp2_hw((x[u] - M) * kLog2e);
+        ws += w;
+        acc += skip ? z : w * v[u];
       }
     }
+    part[t] = acc;
+    wpart[t] = ws;
+    __syncthreads();
+    W = 0.f;
+    if (gi == 0) {
+      acc = part[t];
+      W = wpart[t];
+      for (int k = 1; k < NG; ++k) {
+        acc += part[k * ncol + t];
+        W += wpart[k * ncol + t];
+      }
+    }
+  } else {
+    float mx = kNegInf;
+    for (int s = t; s < S_row; s += 256) mx = fmaxf(mx, pl[(size_t)s * ls]);
+    M = block_reduce(mx, red, true);
+    float ws = 0.f;
+    if (M != kNegInf)
+      for (int s = t; s < S_row; s += 256) {
+        const float x = pl[(size_t)s * ls];
+        ws += (x == kNegInf) ? 0.f : exp2_hw((x - M) * kLog2e);
+      }
+    W = block_reduce(ws, red, false);
+    if (M != kNegInf && gi < NG) {
+      for (int s0 = gi; s0 < S_row; s0 += NG * kCombineUnroll) {
+        f32x4 v[kCombineUnroll];
+        float x[kCombineUnroll];
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+          const int s = s0 + u * NG;
+          const int sc = s < S_row ? s : S_row - 1;
+          x[u] = s < S_row ? pl[(size_t)sc * ls] : kNegInf;
+          v[u] = *reinterpret_cast<const f32x4*>(po + (size_t)sc * os + 4 * c);
+        }
+#pragma unroll
+        for (int u = 0; u < kCombineUnroll; ++u) {
+          const float w = exp2_hw((x[u] - M) * kLog2e);
+          acc += (x[u] == kNegInf) ? z : w * v[u];
+        }
+      }
+    }
+    part[t] = acc;
+    __syncthreads();
+    if (gi == 0) {
+      acc = part[t];
+      for (int k = 1; k < NG; ++k) acc += part[k * ncol + t];
+    }
   }
-  part[t] = acc;
-  __syncthreads();
   if (gi == 0) {
-    f32x4 sum = part[t];
-    for (int k = 1; k < NG; ++k) sum += part[k * ncol + t];
-    const float inv = empty ? 0.f : 1.f / W;
-    sum *= inv;
+    const bool empty = M == kNegInf || !(W > 0.f);
+    const f32x4 sum = empty ? z : acc * (1.f / W);
     if (a.out_bf16) {
       u32x2 w2 = {pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
       *reinterpret_cast<u32x2*>((uint16_t*)a.o + (size_t)row * D + 4 * c) = w2;
@@ -138,6 +217,7 @@ struct MergeStatsArgs {
   int head_dim;
   int out_bf16;
   int mode;
+  int cols;              // float4 columns per workgroup, as for the combine
 };
 
 __device__ __forceinline__ void store_row4(const MergeStatsArgs& a, int row, int c, f32x4 v) {
@@ -150,7 +230,7 @@ __device__ __forceinline__ void store_row4(const MergeStatsArgs& a, int row, int
   }
 }
 
-// Grid: (rows, ceil(D / 128)); 256 threads.
+// Grid: (rows, ceil(D / (4 cols))); 256 threads.
 __global__ __launch_bounds__(256) void miattn_merge_stats_kernel(MergeStatsArgs a) {
   __shared__ float red[256];
   __shared__ f32x4 part[256];
@@ -158,8 +238,8 @@ __global__ __launch_bounds__(256) void miattn_merge_stats_kernel(MergeStatsArgs 
   const int S = a.num_splits;
   const int D = a.head_dim;
   const int DQ = D / 4;
-  const int col0 = blockIdx.y * kCombineCols;
-  const int ncol = DQ - col0 < kCombineCols ? DQ - col0 : kCombineCols;
+  const int col0 = blockIdx.y * a.cols;
+  const int ncol = DQ - col0 < a.cols ? DQ - col0 : a.cols;
   const int t = threadIdx.x;
   const float* pm = a.part_m + (size_t)row * S;
   const float* pl = a.part_l + (size_t)row * S;

@@ -47,6 +47,7 @@
 // O^T += V^T . P^T; the V^T operand comes from the page staged in LDS and read
 // back with the transposing ds_read_b64_tr_b16.
 #pragma once
+#include "balance.h"
 #include "common.h"
 
 namespace miattn {
@@ -75,6 +76,7 @@ struct DecodeArgs {
   int record;                   // STUDY: split record 0-3
   int rounded_l;                // STUDY: normaliser sums the rounded weights
   int tile_shift;               // RR: log2(pages per tile)
+  int balance_units;            // > 0: length-proportional groups (balance.h), U per head group
 };
 
 constexpr int kDecodeWaves = 8;
@@ -116,10 +118,23 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
   const int WPH = kDecodeWaves / HW;                 // waves per kv head
   const int n_hg = a.num_kv_heads / HW;
   const int lin = blockIdx.x;
-  const int per_split = n_hg * a.batch;
-  const int split = lin / per_split;
-  const int hg = (lin % per_split) % n_hg;
-  const int b = (lin % per_split) / n_hg;
+  // Length-proportional groups (fast path only): the grid is head group
+  // fastest, then group index; groups past the plan's last exit.
+  const bool balanced = !STUDY && a.balance_units > 0;
+  int split, hg, b;
+  SplitPlan plan = {0, 0, 0, 0, 0, 1};
+  if (balanced) {
+    hg = lin % n_hg;
+    split = lin / n_hg;
+    plan = balanced_plan(a.seq_lens, a.batch, a.max_pages, a.balance_units, split, true);
+    if (plan.b < 0) return;   // uniform over the workgroup
+    b = plan.b;
+  } else {
+    const int per_split = n_hg * a.batch;
+    split = lin / per_split;
+    hg = (lin % per_split) % n_hg;
+    b = (lin % per_split) / n_hg;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = hg * HW + wave / WPH;                // this wave's kv head
@@ -139,12 +154,19 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
   int np_split;
   int p0 = 0;
   if constexpr (!RR) {
-    // every split of every sequence covers the same page budget, sized from
-    // the block-table width, so sequences of different lengths balance
-    const int pps = (a.max_pages + S - 1) / S;
-    p0 = split * pps < n_pages ? split * pps : n_pages;
-    const int p1 = p0 + pps < n_pages ? p0 + pps : n_pages;
-    np_split = p1 - p0;
+    if (balanced) {
+      // group plan.s: C consecutive pages (the last group of a sequence fewer)
+      const int pps = plan.group_pages;
+      p0 = plan.s * pps < n_pages ? plan.s * pps : n_pages;
+      np_split = (p0 + pps < n_pages ? p0 + pps : n_pages) - p0;
+    } else {
+      // every split of every sequence covers the same page budget, sized
+      // from the block-table width
+      const int pps = (a.max_pages + S - 1) / S;
+      p0 = split * pps < n_pages ? split * pps : n_pages;
+      const int p1 = p0 + pps < n_pages ? p0 + pps : n_pages;
+      np_split = p1 - p0;
+    }
   } else {
     const int sh = a.tile_shift;
     const int n_tiles = (n_pages + (1 << sh) - 1) >> sh;
@@ -368,13 +390,16 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
     }
     o *= inv;
     const float lse = empty ? kNegInf : (M + log2_hw(Lsum)) * kLn2;
-    if (!STUDY && S == 1) {
+    if (!STUDY && !balanced && S == 1) {
       u32x2 w2 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
       *reinterpret_cast<u32x2*>(a.o + row * D + d4) = w2;
       if (a.lse != nullptr && d4 == 0) a.lse[row] = lse;
     } else {
-      *reinterpret_cast<f32x4*>(a.part_o + (row * S + split) * D + d4) = o;
-      if (d4 == 0) a.part_lse[row * S + split] = lse;
+      // partial slot: [row][split], or [group][head] for balanced groups
+      const size_t slot = balanced ? (size_t)split * a.num_q_heads + (row - (size_t)b * a.num_q_heads)
+                                   : row * S + split;
+      *reinterpret_cast<f32x4*>(a.part_o + slot * D + d4) = o;
+      if (d4 == 0) a.part_lse[slot] = lse;
     }
   }
 }

@@ -105,7 +105,10 @@ long fwd_setup(miattn::FwdArgs& a, int num_seqs, int max_seqlen, int num_q_heads
 
 template <int D, bool RR = false, bool PF16 = false, bool STUDY = false>
 void launch_decode(const miattn::DecodeArgs& a, hipStream_t st) {
-  const unsigned grid = (unsigned)((long)a.num_splits * (a.num_kv_heads / a.heads_per_wg) * a.batch);
+  // contiguous splits: splits x head groups x sequences; balanced groups: at
+  // most units + batch groups per head group (the surplus exits at once)
+  const long groups = a.balance_units > 0 ? (long)a.balance_units + a.batch : (long)a.num_splits * a.batch;
+  const unsigned grid = (unsigned)(groups * (a.num_kv_heads / a.heads_per_wg));
   hipLaunchKernelGGL((miattn::miattn_decode_split_kernel<D, RR, PF16, STUDY>), dim3(grid),
                      dim3(miattn::kDecodeThreads), 0, st, a);
 }
@@ -262,9 +265,10 @@ int miattn_decode_pick_splits(int batch, int num_kv_heads, int max_seq_len) {
 }
 
 size_t miattn_decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int num_splits) {
-  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits <= 1) return 0;
-  const size_t rows = (size_t)batch * num_q_heads;
-  const size_t bytes = rows * (size_t)num_splits * ((size_t)head_dim + 1) * sizeof(float);
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits == 1 || num_splits < 0) return 0;
+  // num_splits == 0: the library policy, at most kCUs + batch groups per head
+  const size_t groups = num_splits == 0 ? (size_t)kCUs + batch : (size_t)batch * num_splits;
+  const size_t bytes = groups * num_q_heads * ((size_t)head_dim + 1) * sizeof(float);
   return (bytes + 255) & ~(size_t)255;
 }
 
@@ -390,10 +394,11 @@ int miattn_attn_combine(const float* partial_o, const float* partial_lse, int ro
   if (!partial_o || !partial_lse || !o) return fail(MIATTN_ERR_INVALID_ARG, "attn_combine: null pointer");
   const int dev = current_device();
   if (dev < 0) return dev;
-  miattn::CombineArgs a;
+  miattn::CombineArgs a{};
   a.part_o = partial_o; a.part_lse = partial_lse; a.o = o; a.lse = lse;
   a.rows = rows; a.num_splits = num_splits; a.head_dim = head_dim; a.out_bf16 = out_dtype == MIATTN_BF16;
-  const unsigned chunks = (unsigned)((head_dim / 4 + miattn::kCombineCols - 1) / miattn::kCombineCols);
+  a.cols = miattn::combine_cols(rows, head_dim);
+  const unsigned chunks = (unsigned)((head_dim / 4 + a.cols - 1) / a.cols);
   hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3(rows, chunks), dim3(256), 0, (hipStream_t)stream, a);
   const int r = check_launch("combine");
   return r ? r : ok();
@@ -416,12 +421,23 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
     if (r) return r;
   }
   int S = num_splits;
-  if (S == 0) S = miattn_decode_pick_splits(batch, num_kv_heads, max_pages_per_seq * MIATTN_PAGE_SIZE);
+  // num_splits == 0: where the split-count policy would split at all, the
+  // library splits each sequence into groups proportional to its length
+  // (units groups per kv-head group in all), else one group per sequence
+  int units = 0;
+  const int n_hg = num_kv_heads / decode_heads_per_wg(num_kv_heads);
+  if (S == 0) {
+    S = miattn_decode_pick_splits(batch, num_kv_heads, max_pages_per_seq * MIATTN_PAGE_SIZE);
+    // (a single sequence's groups are the contiguous splits already)
+    if (S > 1 && batch > 1) units = kCUs / n_hg > 1 ? kCUs / n_hg : 1;
+  }
   if (S > max_pages_per_seq) S = max_pages_per_seq;   // more splits than pages would only add empty groups
   if (S < 1) S = 1;
-  if ((long)S * num_kv_heads * batch > 0x7fffffffL)
+  if ((long)S * num_kv_heads * batch > 0x7fffffffL || (long)(units + batch) * num_kv_heads > 0x7fffffffL)
     return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: splits * Hkv * batch too large");
-  const size_t need = miattn_decode_workspace_bytes(batch, num_q_heads, head_dim, S);
+  const size_t need = units > 0 ? ((((size_t)units + batch) * num_q_heads * ((size_t)head_dim + 1) * sizeof(float) + 255)
+                                   & ~(size_t)255)
+                                : miattn_decode_workspace_bytes(batch, num_q_heads, head_dim, S);
   if (workspace != nullptr && workspace_bytes < need)
     return fail(MIATTN_ERR_WORKSPACE, "attn_decode_paged: workspace of %zu bytes, need %zu", workspace_bytes,
                 need);
@@ -437,8 +453,11 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
   a.q = (const uint16_t*)q; a.k_cache = (const uint16_t*)k_cache; a.v_cache = (const uint16_t*)v_cache;
   a.block_table = block_table; a.seq_lens = seq_lens; a.batch = batch;
   const size_t rows = (size_t)batch * num_q_heads;
+  // partials: [rows][S] (contiguous splits) or [units + batch][Hq] (groups)
+  const size_t slots = units > 0 ? ((size_t)units + batch) * num_q_heads : rows * (size_t)S;
   a.part_o = S > 1 ? (float*)ws : nullptr;
-  a.part_lse = S > 1 ? (float*)ws + rows * (size_t)S * head_dim : nullptr;
+  a.part_lse = S > 1 ? (float*)ws + slots * head_dim : nullptr;
+  a.balance_units = units;
   a.o = (uint16_t*)o; a.lse = lse;
   a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
   a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = num_q_heads / num_kv_heads;
@@ -452,10 +471,15 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
   int r = check_launch("decode split");
   if (r) return r;
   if (S > 1) {
-    miattn::CombineArgs c;
+    miattn::CombineArgs c{};
     c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
     c.rows = (int)rows; c.num_splits = S; c.head_dim = head_dim; c.out_bf16 = 1;
-    const unsigned chunks = (unsigned)((head_dim / 4 + miattn::kCombineCols - 1) / miattn::kCombineCols);
+    if (units > 0) {
+      c.seq_lens = seq_lens; c.batch = batch; c.max_pages = max_pages_per_seq;
+      c.balance_units = units; c.num_q_heads = num_q_heads;
+    }
+    c.cols = miattn::combine_cols((long)rows, head_dim);
+    const unsigned chunks = (unsigned)((head_dim / 4 + c.cols - 1) / c.cols);
     hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3((unsigned)rows, chunks), dim3(256), 0, st, c);
     r = check_launch("combine");
     if (r) return r;
@@ -631,17 +655,20 @@ int miattn_attn_decode_paged_numerics(const void* q, const void* k_cache, const 
   }
   int r = check_launch("decode split (numerics)");
   if (r) return r;
-  const unsigned chunks = (unsigned)((head_dim / 4 + miattn::kCombineCols - 1) / miattn::kCombineCols);
+  const int cols = miattn::combine_cols((long)rows, head_dim);
+  const unsigned chunks = (unsigned)((head_dim / 4 + cols - 1) / cols);
   if (record == 0) {
-    miattn::CombineArgs c;
+    miattn::CombineArgs c{};
+    c.cols = cols;
     c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
     c.rows = (int)rows; c.num_splits = S; c.head_dim = head_dim; c.out_bf16 = out_dtype == MIATTN_BF16;
     hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3((unsigned)rows, chunks), dim3(256), 0, st, c);
   } else {
-    miattn::MergeStatsArgs m;
+    miattn::MergeStatsArgs m{};
     m.part_o = a.part_o; m.part_m = a.part_m; m.part_l = a.part_l; m.o = o; m.lse = lse;
     m.rows = (int)rows; m.num_splits = S; m.head_dim = head_dim; m.out_bf16 = out_dtype == MIATTN_BF16;
     m.mode = record;
+    m.cols = cols;
     hipLaunchKernelGGL(miattn::miattn_merge_stats_kernel, dim3((unsigned)rows, chunks), dim3(256), 0, st, m);
   }
   r = check_launch("merge (numerics)");

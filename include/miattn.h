@@ -143,10 +143,17 @@ int miattn_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cach
  *            may be NULL). A sequence of length 0 gives o = 0, lse = -inf.
  *   page_size must be MIATTN_PAGE_SIZE; head_dim 64, 128 or 256; Hq/Hkv <= 8
  *            (MIATTN_ERR_UNSUPPORTED otherwise).
- *   num_splits: >= 1 to fix the split count, 0 to let the library choose
- *            (miattn_decode_pick_splits); counts above max_pages_per_seq are
- *            lowered to it. Bitwise reproducibility holds for a fixed split
- *            count.
+ *   num_splits: >= 1 to fix the split count (the contiguous groups above;
+ *            counts above max_pages_per_seq are lowered to it), or 0 for the
+ *            library's plan: where miattn_decode_pick_splits would split at all
+ *            and the batch holds more than one sequence, every group holds the
+ *            same number C of consecutive pages of one sequence (its last group
+ *            fewer), C being the smallest size for which the batch needs at
+ *            most 256 / (kv-head groups of a workgroup) groups, so sequences of
+ *            any length mix share the work evenly (the plan depends on
+ *            seq_lens only); otherwise the pick_splits count of contiguous
+ *            groups. Bitwise reproducibility holds for a fixed num_splits and
+ *            fixed inputs.
  *   workspace / workspace_bytes: device scratch for the split partials
  *            (miattn_decode_workspace_bytes bytes). workspace == NULL uses a
  *            buffer the library allocates and caches per device (grown on
@@ -181,8 +188,9 @@ int miattn_attn_combine(const float* partial_o, const float* partial_lse, int ro
                         int num_splits, int head_dim, void* o, float* lse, int out_dtype,
                         void* stream);
 
-/* Bytes of workspace miattn_attn_decode_paged needs for the partials
- * (0 when num_splits <= 1). */
+/* Bytes of workspace miattn_attn_decode_paged needs for the partials:
+ * 0 when num_splits == 1; for num_splits == 0 an upper bound for the
+ * library's plan ((256 + batch) groups per query head). */
 size_t miattn_decode_workspace_bytes(int batch, int num_q_heads, int head_dim, int num_splits);
 
 /*

@@ -164,7 +164,7 @@ def test_caller_workspace():
         run(case, 4, workspace=small)
 
 
-@pytest.mark.parametrize("S", [2, 4, 16])
+@pytest.mark.parametrize("S", [0, 2, 4, 16])
 def test_library_and_caller_workspace_agree(S):
     case = synth.make_decode(3, 11, [1, 900, 37, 2048, 513, 64, 17, 1500], 32, 8, 128, 1 / math.sqrt(128),
                              shuffle=True, tail="nan", name="workspace_paths")
@@ -193,3 +193,34 @@ def test_repeatable_with_other_shapes_in_between():
     Ob, Lb = reference(b)
     assert_bf16_close(host(ob), Ob, "interleaved batch")
     assert_lse_close(host(lb), Lb, "interleaved batch")
+
+
+def test_policy_groups_follow_lengths():
+    # num_splits = 0 on a batch the split-count policy splits: groups
+    # proportional to each sequence's length, an empty sequence, a one-token
+    # one; parity, repeatability, and agreement with fixed contiguous splits
+    lens = [4096, 512, 0, 1, 3000, 700, 4095, 16, 2048, 1500] * 4
+    case = synth.make_decode(3, 14, lens, 32, 8, 128, 1 / math.sqrt(128), shuffle=True, tail="nan",
+                             name="policy_groups")
+    assert mi.decode_pick_splits(case.batch, 8, case.max_pages * 16) > 1
+    dev = to_dev(case)
+    O, L = reference(case)
+    o1, l1 = run(case, 0, dev)
+    assert_bf16_close(host(o1), O, "policy groups")
+    assert_lse_close(host(l1), L, "policy groups")
+    o2, l2 = run(case, 0, dev)
+    assert bitwise_equal(o1, o2) and bitwise_equal(l1, l2)
+    o4, _ = run(case, 4, dev)
+    mx, mean = errors(host(o1), host(o4))
+    assert mx <= 1e-2 and mean <= 1e-3
+
+
+def test_policy_groups_of_one_sequence_are_the_contiguous_splits():
+    # one sequence: the policy's 256 groups are exactly the 256 contiguous
+    # splits of the table width, so the bits agree
+    case = synth.config4(ctx=16384, seed=3)
+    assert mi.decode_pick_splits(1, case.num_kv_heads, case.max_pages * 16) == 256
+    dev = to_dev(case)
+    o0, l0 = run(case, 0, dev)
+    o1, l1 = run(case, 256, dev)
+    assert bitwise_equal(o0, o1) and bitwise_equal(l0, l1)
