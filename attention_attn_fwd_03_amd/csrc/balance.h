@@ -135,4 +135,22 @@ __device__ inline SplitPlan balanced_plan(const int32_t* seq_lens, int batch, in
   return p;
 }
 
+// Writes the plan's per-sequence table: start_b at table[b], s_b at
+// table[batch + b] (one wave; C from balanced_plan).
+__device__ inline void write_plan_table(const int32_t* seq_lens, int batch, int max_pages, int C, int32_t* table) {
+  const int lane = lane_id();
+  int run = 0;
+  for (int base = 0; base < batch; base += 64) {
+    const int i = base + lane;
+    const int n = i < batch ? plan_pages(seq_lens, i, max_pages) : 0;
+    const int s = (n + C - 1) / C;
+    const int incl = wave_incl_scan_i32(s, lane);
+    if (i < batch) {
+      table[i] = run + incl - s;
+      table[batch + i] = s;
+    }
+    run += __builtin_amdgcn_readlane(incl, 63);
+  }
+}
+
 }  // namespace miattn

@@ -26,12 +26,11 @@ struct CombineArgs {
   int out_bf16;
   int cols;               // float4 columns per workgroup (4 .. 32, power of two)
   // decode partials in balanced groups (balance.h): row = b * Hq + h reads
-  // groups start_b .. start_b + s_b - 1 at [group][Hq][D]; seq_lens == null:
-  // the [rows][num_splits][D] layout
-  const int32_t* seq_lens;
+  // groups start_b .. start_b + s_b - 1 at [group][Hq][D], start_b and s_b
+  // from plan_table ([2][batch], written by the split kernel); null: the
+  // [rows][num_splits][D] layout
+  const int32_t* plan_table;
   int batch;
-  int max_pages;
-  int balance_units;
   int num_q_heads;
 };
 
@@ -86,11 +85,11 @@ __global__ __launch_bounds__(256) void miattn_combine_kernel(CombineArgs a) {
   const float* pl = a.part_lse + (size_t)row * S;
   const float* po = a.part_o + (size_t)row * S * D;
   size_t ls = 1, os = D;
-  if (a.seq_lens != nullptr) {
+  if (a.plan_table != nullptr) {
     const int Hq = a.num_q_heads;
-    const SplitPlan p = balanced_plan(a.seq_lens, a.batch, a.max_pages, a.balance_units, row / Hq, false);
-    S_row = p.count;
-    const size_t first = (size_t)p.start * Hq + row % Hq;
+    const int b = row / Hq;
+    S_row = a.plan_table[a.batch + b];
+    const size_t first = (size_t)a.plan_table[b] * Hq + row % Hq;
     pl = a.part_lse + first;
     po = a.part_o + first * D;
     ls = Hq;

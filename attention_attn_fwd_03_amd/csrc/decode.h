@@ -77,6 +77,7 @@ struct DecodeArgs {
   int rounded_l;                // STUDY: normaliser sums the rounded weights
   int tile_shift;               // RR: log2(pages per tile)
   int balance_units;            // > 0: length-proportional groups (balance.h), U per head group
+  int32_t* plan_table;          // balanced: [2][batch] first group and group count per sequence
 };
 
 constexpr int kDecodeWaves = 8;
@@ -127,6 +128,9 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
     hg = lin % n_hg;
     split = lin / n_hg;
     plan = balanced_plan(a.seq_lens, a.batch, a.max_pages, a.balance_units, split, true);
+    // the first workgroup publishes the per-sequence table for the combine
+    if (lin == 0 && threadIdx.x < 64)
+      write_plan_table(a.seq_lens, a.batch, a.max_pages, plan.group_pages, a.plan_table);
     if (plan.b < 0) return;   // uniform over the workgroup
     b = plan.b;
   } else {

@@ -268,7 +268,8 @@ size_t miattn_decode_workspace_bytes(int batch, int num_q_heads, int head_dim, i
   if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || num_splits == 1 || num_splits < 0) return 0;
   // num_splits == 0: the library policy, at most kCUs + batch groups per head
   const size_t groups = num_splits == 0 ? (size_t)kCUs + batch : (size_t)batch * num_splits;
-  const size_t bytes = groups * num_q_heads * ((size_t)head_dim + 1) * sizeof(float);
+  const size_t bytes = groups * num_q_heads * ((size_t)head_dim + 1) * sizeof(float) +
+                       (num_splits == 0 ? 2 * (size_t)batch * sizeof(int32_t) : 0);
   return (bytes + 255) & ~(size_t)255;
 }
 
@@ -435,8 +436,9 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
   if (S < 1) S = 1;
   if ((long)S * num_kv_heads * batch > 0x7fffffffL || (long)(units + batch) * num_kv_heads > 0x7fffffffL)
     return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: splits * Hkv * batch too large");
-  const size_t need = units > 0 ? ((((size_t)units + batch) * num_q_heads * ((size_t)head_dim + 1) * sizeof(float) + 255)
-                                   & ~(size_t)255)
+  // balanced groups: partials of units + batch groups, then the plan table
+  const size_t need = units > 0 ? ((((size_t)units + batch) * num_q_heads * ((size_t)head_dim + 1) * sizeof(float) +
+                                    2 * (size_t)batch * sizeof(int32_t) + 255) & ~(size_t)255)
                                 : miattn_decode_workspace_bytes(batch, num_q_heads, head_dim, S);
   if (workspace != nullptr && workspace_bytes < need)
     return fail(MIATTN_ERR_WORKSPACE, "attn_decode_paged: workspace of %zu bytes, need %zu", workspace_bytes,
@@ -458,6 +460,7 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
   a.part_o = S > 1 ? (float*)ws : nullptr;
   a.part_lse = S > 1 ? (float*)ws + slots * head_dim : nullptr;
   a.balance_units = units;
+  a.plan_table = units > 0 ? (int32_t*)(a.part_lse + slots) : nullptr;
   a.o = (uint16_t*)o; a.lse = lse;
   a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
   a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = num_q_heads / num_kv_heads;
@@ -475,8 +478,7 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
     c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
     c.rows = (int)rows; c.num_splits = S; c.head_dim = head_dim; c.out_bf16 = 1;
     if (units > 0) {
-      c.seq_lens = seq_lens; c.batch = batch; c.max_pages = max_pages_per_seq;
-      c.balance_units = units; c.num_q_heads = num_q_heads;
+      c.plan_table = a.plan_table; c.batch = batch; c.num_q_heads = num_q_heads;
     }
     c.cols = miattn::combine_cols((long)rows, head_dim);
     const unsigned chunks = (unsigned)((head_dim / 4 + c.cols - 1) / c.cols);
