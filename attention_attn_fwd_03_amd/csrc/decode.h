@@ -90,8 +90,8 @@ constexpr float kRescaleThreshold = 8.0f;
 
 template <int D>
 struct DecodeSmem {
-  static constexpr int kRowElems = D + 8;                         // padded V row (bf16)
-  static constexpr int kStageBytes = kDecodeWaves * kPage * kRowElems * 2;
+  static constexpr int kRowElems = D + 8;                         // padded K/V row (bf16)
+  static constexpr int kStageBytes = kDecodeWaves * 2 * kPage * kRowElems * 2;   // K and V per wave
   static constexpr int kMergeBytes = kDecodeWaves * kDecodeMaxGroup * D * 4;
   static constexpr int kBytes = (kStageBytes > kMergeBytes ? kStageBytes : kMergeBytes)
                                 + 2 * kDecodeWaves * 16 * 4;      // m and l per wave and head
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = hg * HW + wave / WPH;                // this wave's kv head
   const int phase = wave % WPH;                      // this wave's pages: phase + WPH i
-  const int tok = lane & 15;     // token row for K/V loads and the S^T A operand
+  const int tok = lane & 15;     // token row of the S^T A operand
   const int quad = lane >> 4;    // 0..3
   const int hl = lane & 15;      // query head (within the group) owned by this lane
   const int G = a.group;
@@ -229,39 +229,58 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
 #pragma unroll
   for (int i = 0; i < NDT; ++i) acc[i] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  MIATTN_LDS uint16_t* vstage = (MIATTN_LDS uint16_t*)(smem) + wave * kPage * Smem::kRowElems;
+  MIATTN_LDS uint16_t* vstage = (MIATTN_LDS uint16_t*)(smem) + wave * 2 * kPage * Smem::kRowElems;
+  MIATTN_LDS uint16_t* kstage = vstage + kPage * Smem::kRowElems;
 
-  // K/V rows of the wave's i-th page (token `tok`, this lane's d chunks);
-  // returns the physical page (-1: contributes nothing). The page must lie in
-  // the current block-table window. Loads never branch: an invalid page reads
-  // page 0 and its values are masked (K) or zeroed (V) before use.
+  // Page copies move whole rows: copy j reads rows RPI j + lrow of the page,
+  // CPR 16-byte chunks per row (chunk lch of the row per lane), so each
+  // instruction fetches full 128-byte lines. The data is read exactly once,
+  // hence non-temporal loads.
+  constexpr int CPR = D / 8;         // chunks per row
+  constexpr int RPI = 64 / CPR;      // rows per copy; NKK copies cover the 16 rows
+  const int lrow = lane / CPR;
+  const int lch = lane % CPR;
+
+  // K/V rows of the wave's i-th page into registers; returns the physical
+  // page (-1: contributes nothing). The page must lie in the current
+  // block-table window. Loads never branch: an invalid page reads page 0 and
+  // its values are masked (K) or zeroed (V) before use.
   auto load_page = [&](int i, u32x4* kb, u32x4* vb) -> int {
     const int pp = phys_page(i);
-    const uint16_t* kp = a.k_cache + (size_t)(pp >= 0 ? pp : 0) * page_stride + (size_t)tok * row_stride
-                         + (size_t)g * D + 8 * quad;
+    const uint16_t* kp = a.k_cache + (size_t)(pp >= 0 ? pp : 0) * page_stride + (size_t)lrow * row_stride
+                         + (size_t)g * D + 8 * lch;
     const uint16_t* vp = a.v_cache + (kp - a.k_cache);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      kb[kk] = ld16(kp + 32 * kk);
-      vb[kk] = ld16(vp + 32 * kk);
+    for (int j = 0; j < NKK; ++j) {
+      kb[j] = ld16_stream(kp + (size_t)(RPI * j) * row_stride);
+      vb[j] = ld16_stream(vp + (size_t)(RPI * j) * row_stride);
     }
     return pp;
   };
 
-  // Page i: S^T = K Q^T, stage V in LDS (rows of tokens past the sequence end
-  // or of an invalid page as zeros); the caller may then refill kb/vb.
-  auto scores = [&](int i, bool page_ok, const u32x4* kb, const u32x4* vb) -> f32x4 {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kb[kk]), as_bf16x8(qop[kk]), s, 0, 0, 0);
+  // Page i's registers into the wave's LDS rows (V rows of tokens past the
+  // sequence end or of an invalid page as zeros); the caller may then refill
+  // kb/vb.
+  auto stage = [&](int i, bool page_ok, const u32x4* kb, const u32x4* vb) {
     const int lp = logical_page(phase + WPH * i);
-    const bool row_ok = page_ok && lp * kPage + tok < L;
     const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
+    for (int j = 0; j < NKK; ++j) {
+      const int row = RPI * j + lrow;
+      const bool row_ok = page_ok && lp * kPage + row < L;
+      lds_st16(kstage + row * Smem::kRowElems + 8 * lch, kb[j]);
+      lds_st16(vstage + row * Smem::kRowElems + 8 * lch,
+               row_ok ? (PF16 ? bf16x8_to_f16x8(vb[j]) : vb[j]) : z);
+    }
+  };
+  // S^T = K Q^T for the staged page: token tok, d = 32 kk + 8 quad .. +7.
+  auto scores = [&]() -> f32x4 {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    const MIATTN_LDS uint16_t* kr = kstage + tok * Smem::kRowElems + 8 * quad;
+#pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      lds_st16(vstage + tok * Smem::kRowElems + 32 * kk + 8 * quad,
-               row_ok ? (PF16 ? bf16x8_to_f16x8(vb[kk]) : vb[kk]) : z);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(lds_ld16(kr + 32 * kk)), as_bf16x8(qop[kk]), s, 0, 0,
+                                                  0);
     return s;
   };
   // Online softmax for page i and O^T += V^T P^T from the staged V.
@@ -330,10 +349,10 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
         const int ii = i0 + j;                  // index inside the window
         const bool live = ii < n_in;            // uniform
         const bool ok_i = live && pp_buf[j] >= 0;
-        const f32x4 s = scores(w0 + ii, ok_i, kb[j], vb[j]);
+        stage(w0 + ii, ok_i, kb[j], vb[j]);
         const int nxt = ii + PF < n_in ? ii + PF : n_in - 1;
         pp_buf[j] = load_page(w0 + nxt, kb[j], vb[j]);
-        if (live) accumulate(w0 + ii, s, ok_i);
+        if (live) accumulate(w0 + ii, scores(), ok_i);
       }
     }
   }
