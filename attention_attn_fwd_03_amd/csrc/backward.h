@@ -12,13 +12,13 @@
 //  * prep: Delta = rowsum(dO * O) in fp32, the LSE in log2 units (both in
 //    rows padded by 32 so tile-sized copies stay in bounds), and fp16 copies
 //    of Q, dO, K and V, in one pass over the inputs.
-//  * dK/dV: one workgroup of 4 waves per (kv head, 32 keys, sequence). Every
-//    wave holds the same 32 keys' K and V as MFMA operands and dK^T, dV^T
-//    accumulators in registers, and takes every fourth (query head, 32-query
-//    tile) step of the group, with its own double-buffered Q/dO tiles copied
-//    straight from HBM into LDS; the waves never wait for each other until the
-//    end, where their four partial sums are added through LDS in a fixed
-//    order. Per tile: S = Q K^T and dP = dO V^T (query rows, key columns),
+//  * dK/dV: one workgroup of 4 waves per (kv head, 32 keys, sequence). The
+//    32 keys' K and V sit in LDS (copied once, read back as MFMA operands at
+//    every step); every wave holds dK^T, dV^T accumulators in registers and
+//    takes every fourth (query head, 32-query tile) step of the group, with
+//    its own double-buffered Q/dO tiles copied straight from HBM into LDS; the
+//    waves never wait for each other until the end, where their four partial
+//    sums are added through LDS in a fixed order. Per tile: S = Q K^T and dP = dO V^T (query rows, key columns),
 //    then dV^T += dO^T P and dK^T += Q^T dS: the accumulator registers of P
 //    and dS, rounded to fp16, are the B operand as they stand; dO^T and Q^T
 //    come from the same LDS tile through the transposing read.
@@ -88,21 +88,6 @@ struct BwdTile {
 // no key (-inf) gives +inf, i.e. P = 0.
 __device__ __forceinline__ float lse_to_log2(float lse) {
   return lse == kNegInf ? __builtin_inff() : lse * kLog2e;
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Direct HBM -> LDS copy of 16 bytes per lane (buffer load, LDS form) issued
-// from inline asm: lane i's 16 bytes from base + voff land at LDS byte
-// address lds + 16 i. The compiler does not track these writes, so a loop
-// that reads one LDS buffer while a copy fills the other needs no waits from
-// it; the caller waits (s_waitcnt vmcnt) before reading what was copied.
-// base and lds must be uniform.
-__device__ __forceinline__ void dma16_to_lds_asm(const void* base, uint32_t voff, uint32_t lds) {
-  const uint64_t addr = (uint64_t)base;
-  const i32x4 rs = {(int)(uint32_t)addr, (int)((addr >> 32) & 0xffff), 0x7fffffff, 0x00020000};
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rs) : "memory");
 }
 
 // ---------------------------------------------------------------- prep

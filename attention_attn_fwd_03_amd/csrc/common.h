@@ -94,6 +94,21 @@ __device__ __forceinline__ void dma16_to_lds(const void* base, uint32_t voff, MI
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds, 16, voff, 0, 0, 0);
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Direct HBM -> LDS copy of 16 bytes per lane (buffer load, LDS form) issued
+// from inline asm: lane i's 16 bytes from base + voff land at LDS byte
+// address lds + 16 i. The compiler does not track these writes, so a loop
+// that reads one LDS buffer while a copy fills the other needs no waits from
+// it; the caller waits (s_waitcnt vmcnt) before reading what was copied.
+// base and lds must be uniform.
+__device__ __forceinline__ void dma16_to_lds_asm(const void* base, uint32_t voff, uint32_t lds) {
+  const uint64_t addr = (uint64_t)base;
+  const i32x4 rs = {(int)(uint32_t)addr, (int)((addr >> 32) & 0xffff), 0x7fffffff, 0x00020000};
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds), "v"(voff), "s"(rs) : "memory");
+}
+
 __device__ __forceinline__ u32x4 lds_ld16(const MIATTN_LDS void* p) {
   return *reinterpret_cast<const MIATTN_LDS u32x4*>(p);
 }

@@ -15,6 +15,7 @@
 #include "combine.h"
 #include "decode.h"
 #include "prefill.h"
+#include "prefill_pp.h"
 
 namespace {
 
@@ -88,6 +89,19 @@ void launch_fwd_c(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t s
 // query blocks of 32 rows per wave for each head_dim
 constexpr int fwd_qb(int d) { return d >= 256 ? 1 : 1; }
 
+// Dense prefill with head_dim 64 and 128 runs the eight-wave ping-pong kernel
+// (two 32-row groups per query tile); head_dim 256 and the paged (chunked)
+// prefill run the four-wave kernel, which measured faster there.
+constexpr bool fwd_pingpong(int d, bool paged) { return d <= 128 && !paged; }
+
+template <int D>
+void launch_fwd_pp(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t st) {
+  if (causal)
+    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, true>), dim3(grid), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, false>), dim3(grid), dim3(512), 0, st, a);
+}
+
 // bf16 prefill grid: (head slot, query-tile pair, sequence)
 long fwd_setup(miattn::FwdArgs& a, int num_seqs, int max_seqlen, int num_q_heads, int num_kv_heads, int head_dim,
                bool unit_per_tile = false) {
@@ -95,7 +109,7 @@ long fwd_setup(miattn::FwdArgs& a, int num_seqs, int max_seqlen, int num_q_heads
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
   a.heads_per_wg = G >= 4 ? 4 : G;
-  const int QR = 32 * fwd_qb(head_dim) * (4 / a.heads_per_wg);
+  const int QR = 32 * fwd_qb(head_dim) * (4 / a.heads_per_wg) * (fwd_pingpong(head_dim, unit_per_tile) ? 2 : 1);
   const int n_qtiles = (max_seqlen + QR - 1) / QR;
   a.n_pairs = unit_per_tile ? n_qtiles : (n_qtiles + 1) / 2;
   a.n_head_slots = num_kv_heads * (G / a.heads_per_wg);
@@ -329,8 +343,8 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
   if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: problem too large");
   const bool cz = causal != 0;
   switch (head_dim) {
-    case 64: launch_fwd_c<64, fwd_qb(64), 2>(a, (int)grid, cz, st); break;
-    case 128: launch_fwd_c<128, fwd_qb(128), 2>(a, (int)grid, cz, st); break;
+    case 64: launch_fwd_pp<64>(a, (int)grid, cz, st); break;
+    case 128: launch_fwd_pp<128>(a, (int)grid, cz, st); break;
     default: launch_fwd_c<256, fwd_qb(256), 1>(a, (int)grid, cz, st); break;
   }
   const int r = check_launch("prefill bf16");

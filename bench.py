@@ -201,7 +201,7 @@ def numerics_timing(torch, mi, dev, bf16, i32, steps: int, warmup: int):
 # kernels whose HBM traffic the counter summary records: key -> (stage run by
 # --only, kernel-name substrings of one launch)
 TRAFFIC_KERNELS = {
-    "prefill_causal_gqa_s4096": ("prefill", ["miattn_prefill_fwd_kernel"]),
+    "prefill_causal_gqa_s4096": ("prefill", ["miattn_prefill_pp_kernel"]),
     "decode_paged_b64": ("decode", ["miattn_decode_split_kernel", "miattn_combine_kernel"]),
     "decode_long_ctx131072": ("long", ["miattn_decode_split_kernel", "miattn_combine_kernel"]),
     "chunked_prefill_8x1024": ("chunked", ["miattn_prefill_fwd_kernel"]),
@@ -272,6 +272,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="untimed steps for this long before the warmup steps: the GPU clock ramps up "
+                         "over the first few hundred milliseconds of sustained load")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = library policy")
     ap.add_argument("--long-splits", type=int, default=0, help="0 = library policy")
@@ -391,10 +394,23 @@ def main():
         mi.attn_decode_paged(Ld["q"], Ld["kc"], Ld["vc"], Ld["bt"], Ld["sl"], scale=lc.scale,
                              num_splits=lsplits, out=Ld["o"], lse=Ld["lse"])
 
+    def settle(fns):
+        # untimed: run the work until the clocks have settled (bounded queue)
+        t_end = time.perf_counter() + args.settle_ms * 1e-3
+        n = 0
+        while time.perf_counter() < t_end:
+            for fn in fns:
+                fn()
+            n += 1
+            if n % 20 == 0:
+                torch.cuda.synchronize()
+        torch.cuda.synchronize()
+
     stages = [prefill, decode, long_decode]
     if args.only is not None:
         f = {"prefill": prefill, "decode": decode, "long": long_decode, "chunked": chunked,
              "backward": backward}[args.only]
+        settle([f])
         for _ in range(args.warmup):
             f()
         torch.cuda.synchronize()
@@ -407,7 +423,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"only": args.only, "ms": e0.elapsed_time(e1) / args.steps}), flush=True)
         return
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    print(f"[bench] settle {args.settle_ms:.0f} ms, warmup {args.warmup}", file=sys.stderr, flush=True)
+    settle(stages)
     for _ in range(args.warmup):
         for f in stages:
             f()
@@ -517,7 +534,7 @@ def main():
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "miattn_prefill_fwd_kernel<128,1,2,true>",
+                     "kernel": "miattn_prefill_pp_kernel<128, true>",
                      "per_launch_work": f"{fl_pre:.6g} FLOP"},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs_long, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(gbs_long / PEAK_HBM_GBS, 4),
