@@ -268,6 +268,19 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();   // the K/V block copied by all four waves
 
+  // the 32 keys' K and V operands stay in registers for the whole loop
+  // (lane: key lane%32, d = 16 kk + 8 half + 0..7)
+  u32x4 kreg[NKK], vreg[NKK];
+  {
+    const int r = lane & 31;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int o = r * (2 * D) + 16 * ((2 * kk + half) ^ TL::swz(r));
+      kreg[kk] = lds_ld16(k_l + o);
+      vreg[kk] = lds_ld16(v_l + o);
+    }
+  }
+
   // one loop body for both buffers (a copy per buffer would give the
   // accumulators a different register home in each and copies between them)
   for (int i = 0; i < n_mine; ++i) {
@@ -301,41 +314,44 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
       // operands of step kk + 1 are read while step kk's products issue
       const int r = lane & 31;
       auto so = [&](int kk) { return r * (2 * D) + 16 * ((2 * kk + half) ^ TL::swz(r)); };
-      u32x4 oq = lds_ld16(ql + so(0)), ok_ = lds_ld16(k_l + so(0));
-      u32x4 od = lds_ld16(dl_ + so(0)), ov = lds_ld16(v_l + so(0));
+      u32x4 oq = lds_ld16(ql + so(0)), od = lds_ld16(dl_ + so(0));
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 nq = oq, nk = ok_, nd = od, nv = ov;
+        u32x4 nq = oq, nd = od;
         if (kk + 1 < NKK) {
           nq = lds_ld16(ql + so(kk + 1));
-          nk = lds_ld16(k_l + so(kk + 1));
           nd = lds_ld16(dl_ + so(kk + 1));
-          nv = lds_ld16(v_l + so(kk + 1));
         }
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(oq), as_f16x8(ok_), s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(od), as_f16x8(ov), dp, 0, 0, 0);
-        oq = nq; ok_ = nk; od = nd; ov = nv;
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(oq), as_f16x8(kreg[kk]), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(od), as_f16x8(vreg[kk]), dp, 0, 0, 0);
+        oq = nq; od = nd;
       }
     }
     // P = exp2(s c - lse2) and dS = P (dP - Delta), both 0 outside the
     // sequence and (causal) above the diagonal; only tail and diagonal
     // tiles need the mask (uniform test)
+    // The mask goes on the inputs of the exponential, before it, so the
+    // branch does not split the vector work from the products below: a masked
+    // element gets s = -inf and zero LSE and Delta (rows past the sequence end
+    // read stats rows that may hold anything), hence P = 0 and dS =
+    // 0 * dP = 0 (masked rows and keys repeat finite Q/dO/K/V rows).
     const bool need_mask = kb0 + 32 > L || q0 + QT > L || (CAUSAL && kb0 + 31 > q0);
-    float p[16], d[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[e] = exp2_hw(__builtin_fmaf(s[e], c, -l2[e]));
-      d[e] = p[e] * (dp[e] - dl[e]);
-    }
     if (need_mask) {
       asm volatile("" ::: "memory");   // keep this a branch: the common tile skips it
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int qrow = q0 + 8 * (e >> 2) + 4 * half + (e & 3);
         const bool ok = key_ok & (qrow < L) & (!CAUSAL | (key <= qrow));
-        p[e] = ok ? p[e] : 0.f;
-        d[e] = ok ? d[e] : 0.f;
+        s[e] = ok ? s[e] : kNegInf;
+        l2[e] = ok ? l2[e] : 0.f;
+        dl[e] = ok ? dl[e] : 0.f;
       }
+    }
+    float p[16], d[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      p[e] = exp2_hw(__builtin_fmaf(s[e], c, -l2[e]));
+      d[e] = p[e] * (dp[e] - dl[e]);
     }
     u32x4 pw[2], dsw[2];
 #pragma unroll
