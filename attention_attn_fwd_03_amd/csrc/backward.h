@@ -550,6 +550,7 @@ __global__ __launch_bounds__(256, 2) void miattn_bwd_dq_kernel(BwdArgs a) {
     if (kt < n_kt_w) {
       const MIATTN_LDS uint8_t* kl = kbuf(buf);
       const MIATTN_LDS uint8_t* vl = vbuf(buf);
+      const bool need_mask = (kt + 1) * BC > L || (CAUSAL && (kt + 1) * BC - 1 > q0);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         // S^T = K Q^T and dP^T = V dO^T: A = key row 32 kb + lane%32
@@ -567,7 +568,22 @@ __global__ __launch_bounds__(256, 2) void miattn_bwd_dq_kernel(BwdArgs a) {
           dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(lds_ld16(vl + so)), as_f16x8(dop[kk]), dp, 0, 0, 0);
         }
         // dS^T = P^T (dP^T - Delta), 0 outside the sequence and above the
-        // diagonal
+        // diagonal: on tail and diagonal tiles only, masked scores become
+        // -inf (P = 0, dS = 0 * (dP - Delta) = 0; K/V rows past the end repeat
+        // the last one, so dP stays finite). Key of element e: kt BC + 32 kb +
+        // 4 half + (8 (e / 4) + e % 4), kept iff that offset is below lim.
+        // Rows past the end (q_ok false) are computed and never written.
+        if (need_mask) {
+          asm volatile("" ::: "memory");   // keep this a branch: the common tile skips it
+          const int kbase_lane = kt * BC + 32 * kb + 4 * half;
+          int lim = L - kbase_lane;
+          if (CAUSAL) {
+            const int lc = qrow + 1 - kbase_lane;
+            lim = lc < lim ? lc : lim;
+          }
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[e] = (8 * (e >> 2) + (e & 3)) < lim ? s[e] : kNegInf;
+        }
         u32x4 dsw[2];
 #pragma unroll
         for (int e0 = 0; e0 < 16; e0 += 2) {
@@ -575,10 +591,8 @@ __global__ __launch_bounds__(256, 2) void miattn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const int e = e0 + u;
-            const int key = kt * BC + 32 * kb + 8 * (e >> 2) + 4 * half + (e & 3);
-            const bool ok = q_ok && key < L && (!CAUSAL || key <= qrow);
             const float p = exp2_hw(__builtin_fmaf(s[e], c, -l2));
-            d[u] = ok ? p * (dp[e] - dlt) : 0.f;
+            d[u] = p * (dp[e] - dlt);
           }
           dsw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(d[0], d[1]);
         }

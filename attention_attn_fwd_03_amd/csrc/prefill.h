@@ -301,17 +301,22 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
         // mask (diagonal / tail tiles only), raw row max, lazy rescale
         const bool need_mask = (kt + 1) * BC > Lk || (CAUSAL && (kt + 1) * BC - 1 > q0 + off);
         if (need_mask) {
+          // key of score r in block kb: kt BC + 4 half + (32 kb + 8 (r / 4) + r % 4),
+          // kept iff that offset is below lim (compares with immediates, no
+          // per-score registers)
+          const int kbase_lane = kt * BC + 4 * half;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
-            const int qrow = q0 + 32 * qb + (lane & 31);
+            int lim = Lk - kbase_lane;
+            if (CAUSAL) {
+              const int lc = q0 + 32 * qb + (lane & 31) + off + 1 - kbase_lane;
+              lim = lc < lim ? lc : lim;
+            }
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                const int key = kt * BC + 32 * kb + 8 * (r >> 2) + 4 * half + (r & 3);
-                const bool ok = key < Lk && (!CAUSAL || key <= qrow + off);
-                s[qb][kb][r] = ok ? s[qb][kb][r] : kNegInf;
-              }
+              for (int r = 0; r < 16; ++r)
+                s[qb][kb][r] = (32 * kb + 8 * (r >> 2) + (r & 3)) < lim ? s[qb][kb][r] : kNegInf;
           }
         }
         float tmax[QB];
