@@ -223,6 +223,10 @@ int split_rule(long total_tokens, long work_units, long cu_count, long wg_per_cu
 // smallest split count with the best efficiency (the pages' rule settles for
 // 85% of it to save merge work).
 constexpr int kCUs = 256;
+// Smallest batch x block-table width (in tokens) for which num_splits == 0
+// uses the length-proportional plan: measured, the plan's per-workgroup
+// start-up costs 1.5-3.7 us, which only launches of this size repay.
+constexpr long kDecodePlanMinTokens = 1L << 18;
 constexpr int kDecodeWgPerCu = 1;
 constexpr int kMaxSplits = 256;
 constexpr double kPagesRuleThreshold = 0.85;
@@ -436,15 +440,22 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
     if (r) return r;
   }
   int S = num_splits;
-  // num_splits == 0: where the split-count policy would split at all, the
-  // library splits each sequence into groups proportional to its length
-  // (units groups per kv-head group in all), else one group per sequence
+  // num_splits == 0: where the split-count policy would split at all and the
+  // launch is large (batch x table width >= kDecodePlanMinTokens), the library
+  // splits each sequence into groups proportional to its length (units groups
+  // per kv-head group in all); otherwise the policy's contiguous splits
   int units = 0;
   const int n_hg = num_kv_heads / decode_heads_per_wg(num_kv_heads);
   if (S == 0) {
     S = miattn_decode_pick_splits(batch, num_kv_heads, max_pages_per_seq * MIATTN_PAGE_SIZE);
-    // (a single sequence's groups are the contiguous splits already)
-    if (S > 1 && batch > 1) units = kCUs / n_hg > 1 ? kCUs / n_hg : 1;
+    // (a single sequence's groups are the contiguous splits already; small
+    // launches would pay the plan's start-up, ~2 us, for little balance)
+    if (S > 1 && batch > 1 && (long)batch * max_pages_per_seq * MIATTN_PAGE_SIZE >= kDecodePlanMinTokens)
+      units = kCUs / n_hg > 1 ? kCUs / n_hg : 1;
+    // contiguous groups keep within the workspace bound published for
+    // num_splits == 0 (kCUs + batch groups per head): batch * S <= kCUs + batch
+    else if (S > 1 + kCUs / batch)
+      S = 1 + kCUs / batch;
   }
   if (S > max_pages_per_seq) S = max_pages_per_seq;   // more splits than pages would only add empty groups
   if (S < 1) S = 1;

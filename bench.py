@@ -85,9 +85,10 @@ def cpu_baseline(prefill_case, min_seconds: float = 10.0, max_reps: int = 8):
 
 
 def sweep_splits(torch, mi, dev):
-    """Paged decode time for split counts 1, 2, 4, ..., 256 on synthetic caches
-    (seeded device-side normals, shuffled 16-token pages), for the two decode
-    shapes and batch 1-64, contexts 1K-64K (fixed, and uniform in [ctx/8, ctx])."""
+    """Paged decode time for split counts 1, 2, 4, ..., 256 and for the
+    library's own plan (num_splits = 0) on synthetic caches (seeded
+    device-side normals, shuffled 16-token pages), for the two decode shapes
+    and batch 1-64, contexts 1K-64K (fixed, and uniform in [ctx/8, ctx])."""
     import statistics
     g = torch.Generator(device=dev)
     g.manual_seed(0)
@@ -136,11 +137,13 @@ def sweep_splits(torch, mi, dev):
                     pol = mi.decode_pick_splits(B, Hkv, max(lens))
                     cand = sorted({1, 2, 4, 8, 16, 32, 64, 128, 256, pol})
                     res = {S: round(time_it(args, S, D ** -0.5), 1) for S in cand if S <= (max(lens) + 15) // 16}
+                    lib = round(time_it(args, 0, D ** -0.5), 1)   # the library's own plan
                     best = min(res, key=res.get)
                     by = 4 * sum(lens) * Hkv * D
                     print(json.dumps({"shape": {"Hq": Hq, "Hkv": Hkv, "D": D}, "B": B, "ctx": ctx,
                                       "lengths": "uniform [ctx/8, ctx]" if var else "fixed", "policy": pol,
-                                      "us_policy": res.get(pol), "fastest": best, "us_fastest": res[best],
+                                      "us_policy": res.get(pol), "us_library": lib,
+                                      "fastest": best, "us_fastest": res[best],
                                       "GB/s_fastest": round(by / res[best] / 1e3, 1), "us_by_splits": res}),
                           flush=True)
                     del args

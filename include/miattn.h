@@ -145,14 +145,15 @@ int miattn_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cach
  *            (MIATTN_ERR_UNSUPPORTED otherwise).
  *   num_splits: >= 1 to fix the split count (the contiguous groups above;
  *            counts above max_pages_per_seq are lowered to it), or 0 for the
- *            library's plan: where miattn_decode_pick_splits would split at all
- *            and the batch holds more than one sequence, every group holds the
+ *            library's plan: where miattn_decode_pick_splits would split at all,
+ *            the batch holds more than one sequence and batch *
+ *            max_pages_per_seq * page_size >= 2^18, every group holds the
  *            same number C of consecutive pages of one sequence (its last group
  *            fewer), C being the smallest size for which the batch needs at
  *            most 256 / (kv-head groups of a workgroup) groups, so sequences of
  *            any length mix share the work evenly (the plan depends on
  *            seq_lens only); otherwise the pick_splits count of contiguous
- *            groups. Bitwise reproducibility holds for a fixed num_splits and
+ *            groups, at most 1 + 256 / batch. Bitwise reproducibility holds for a fixed num_splits and
  *            fixed inputs.
  *   workspace / workspace_bytes: device scratch for the split partials
  *            (miattn_decode_workspace_bytes bytes). workspace == NULL uses a

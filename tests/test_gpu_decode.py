@@ -196,13 +196,15 @@ def test_repeatable_with_other_shapes_in_between():
 
 
 def test_policy_groups_follow_lengths():
-    # num_splits = 0 on a batch the split-count policy splits: groups
-    # proportional to each sequence's length, an empty sequence, a one-token
-    # one; parity, repeatability, and agreement with fixed contiguous splits
-    lens = [4096, 512, 0, 1, 3000, 700, 4095, 16, 2048, 1500] * 4
+    # num_splits = 0 on a batch the split-count policy splits and large enough
+    # for the length-proportional plan (batch x table width >= 2^18 tokens):
+    # an empty sequence, a one-token one; parity, repeatability, and agreement
+    # with fixed contiguous splits
+    lens = [8192, 512, 0, 1, 6000, 700, 8191, 16, 4096, 1500] * 4
     case = synth.make_decode(3, 14, lens, 32, 8, 128, 1 / math.sqrt(128), shuffle=True, tail="nan",
                              name="policy_groups")
     assert mi.decode_pick_splits(case.batch, 8, case.max_pages * 16) > 1
+    assert case.batch * case.max_pages * 16 >= 1 << 18
     dev = to_dev(case)
     O, L = reference(case)
     o1, l1 = run(case, 0, dev)
@@ -224,3 +226,21 @@ def test_policy_groups_of_one_sequence_are_the_contiguous_splits():
     o0, l0 = run(case, 0, dev)
     o1, l1 = run(case, 256, dev)
     assert bitwise_equal(o0, o1) and bitwise_equal(l0, l1)
+
+
+def test_policy_small_launch_contiguous_within_workspace_bound():
+    # num_splits = 0 below the plan's size threshold: the policy's contiguous
+    # count (256 here) capped at 1 + 256 / batch, so the workspace size
+    # published for num_splits = 0 suffices
+    case = synth.make_decode(3, 15, [4096, 4000, 100], 8, 1, 128, 1 / math.sqrt(128), shuffle=True,
+                             tail="nan", name="small_launch_policy")
+    assert mi.decode_pick_splits(case.batch, 1, case.max_pages * 16) > 1 + 256 // case.batch
+    dev = to_dev(case)
+    O, L = reference(case)
+    ws = torch.empty(mi.decode_workspace_bytes(case.batch, case.num_q_heads, case.head_dim, 0),
+                     dtype=torch.uint8, device=dev[0].device)
+    oc, lc = run(case, 0, dev, workspace=ws)
+    assert_bf16_close(host(oc), O, "small launch, caller workspace")
+    assert_lse_close(host(lc), L, "small launch, caller workspace")
+    ol, ll = run(case, 0, dev)
+    assert bitwise_equal(oc, ol) and bitwise_equal(lc, ll)

@@ -94,6 +94,8 @@ def test_varlen_d256_full_size_sampled():
     ([96], 16, 2, 64, True),        # G = 8: two workgroups per kv head
     ([77, 1, 150], 4, 1, 256, False),
     ([300], 4, 4, 128, True),
+    ([333, 64], 32, 8, 128, False),  # G = 4 non-causal, ragged
+    ([100, 257], 8, 4, 64, False),   # G = 2, D = 64 non-causal
 ])
 def test_shapes(lens, Hq, Hkv, D, causal):
     full_check(synth.make_prefill(20, 0, lens, Hq, Hkv, D, 1 / math.sqrt(D), causal, "bf16",

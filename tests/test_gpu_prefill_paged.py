@@ -58,16 +58,18 @@ def test_config6_shape_against_oracle():
     check(c, True)
 
 
-def test_whole_sequence_chunk_equals_contiguous_prefill_bitwise():
-    # Lq == Lk with pages in order: the same tiles in the same order as the
-    # contiguous kernel, so the bits agree
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (8, 4, 64), (4, 4, 128)])
+def test_whole_sequence_chunk_equals_contiguous_prefill_bitwise(Hq, Hkv, D):
+    # Lq == Lk with pages in order: the paged kernel and the dense one (a
+    # different kernel at D <= 128) visit the same tiles with the same
+    # accumulation orders and softmax rule, so the bits agree
     lens = [700, 33, 256]
-    p = synth.make_prefill(2, 3, lens, 32, 8, 128, 128 ** -0.5, True, "bf16")
+    p = synth.make_prefill(2, 3, lens, Hq, Hkv, D, D ** -0.5, True, "bf16")
     T = sum(lens)
-    k = p.k.reshape(T, 8, 128)
-    v = p.v.reshape(T, 8, 128)
+    k = p.k.reshape(T, Hkv, D)
+    v = p.v.reshape(T, Hkv, D)
     total = sum((L + 15) // 16 for L in lens)
-    kc = np.zeros((total, 16, 8, 128), dtype=np.uint16)
+    kc = np.zeros((total, 16, Hkv, D), dtype=np.uint16)
     vc = np.zeros_like(kc)
     bt = np.full((len(lens), max((L + 15) // 16 for L in lens)), -1, dtype=np.int32)
     page, off = 0, 0
