@@ -106,7 +106,7 @@ __device__ __forceinline__ void dma16_to_lds_asm(const void* base, uint32_t voff
   const uint64_t addr = (uint64_t)base;
   const i32x4 rs = {(int)(uint32_t)addr, (int)((addr >> 32) & 0xffff), 0x7fffffff, 0x00020000};
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
-               :: "s"(lds), "v"(voff), "s"(rs) : "memory");
+               :: "s"(lds), "v"(voff), "s"(rs) : "memory", "m0");
 }
 
 __device__ __forceinline__ u32x4 lds_ld16(const MIATTN_LDS void* p) {
