@@ -94,12 +94,12 @@ constexpr int fwd_qb(int d) { return d >= 256 ? 1 : 1; }
 // prefill run the four-wave kernel, which measured faster there.
 constexpr bool fwd_pingpong(int d, bool paged) { return d <= 128 && !paged; }
 
-template <int D>
+template <int D, int KB>
 void launch_fwd_pp(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t st) {
   if (causal)
-    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, true>), dim3(grid), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, KB, true>), dim3(grid), dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, false>), dim3(grid), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, KB, false>), dim3(grid), dim3(512), 0, st, a);
 }
 
 // bf16 prefill grid: (head slot, query-tile pair, sequence)
@@ -347,8 +347,8 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
   if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: problem too large");
   const bool cz = causal != 0;
   switch (head_dim) {
-    case 64: launch_fwd_pp<64>(a, (int)grid, cz, st); break;
-    case 128: launch_fwd_pp<128>(a, (int)grid, cz, st); break;
+    case 64: launch_fwd_pp<64, 2>(a, (int)grid, cz, st); break;
+    case 128: launch_fwd_pp<128, 2>(a, (int)grid, cz, st); break;
     default: launch_fwd_c<256, fwd_qb(256), 1>(a, (int)grid, cz, st); break;
   }
   const int r = check_launch("prefill bf16");

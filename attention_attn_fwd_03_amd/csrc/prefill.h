@@ -34,7 +34,8 @@
 //    workgroup takes query tiles i and n-1-i of its sequence, so every causal
 //    workgroup does the same work. The head index varies fastest: workgroups
 //    are dealt to the 8 XCDs round robin, so with 8 kv heads each XCD's L2
-//    serves one head's K/V.
+//    serves one head's K/V; the sequence index varies slowest, so the
+//    workgroups resident together read one sequence's K/V.
 #pragma once
 #include <type_traits>
 
@@ -118,10 +119,10 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
   const int lin = blockIdx.x;
   const int hslot = lin % a.n_head_slots;
   const int rest = lin / a.n_head_slots;
-  // paged (chunked prefill): a sequence's tiles are consecutive, so the
-  // workgroups running together on an XCD share one prefix in its L2
-  const int pair = PAGED ? rest % a.n_pairs : rest / a.num_seqs;
-  const int b = PAGED ? rest / a.n_pairs : rest % a.num_seqs;
+  // sequence-major: a sequence's tiles are consecutive, so the workgroups
+  // running together on an XCD share that sequence's K/V in its L2
+  const int pair = rest % a.n_pairs;
+  const int b = rest / a.n_pairs;
   int s0 = a.cu_seqlens[b];
   int s1 = a.cu_seqlens[b + 1];
   s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);

@@ -45,9 +45,8 @@ __device__ __forceinline__ void pp_mfma_reads() {
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int KB, bool CAUSAL>
 __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
-  constexpr int KB = 2;
   constexpr int BC = 32 * KB;   // keys per tile
   using TL = FwdTile<D, KB>;
   constexpr int CH = TL::CH;
@@ -71,8 +70,10 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
   const int lin = blockIdx.x;
   const int hslot = lin % a.n_head_slots;
   const int rest = lin / a.n_head_slots;
-  const int pair = rest / a.num_seqs;
-  const int b = rest % a.num_seqs;
+  // sequence-major: the workgroups resident together read one sequence's
+  // K/V, which then stays in L2
+  const int pair = rest % a.n_pairs;
+  const int b = rest / a.n_pairs;
   int s0 = a.cu_seqlens[b];
   int s1 = a.cu_seqlens[b + 1];
   s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);

@@ -208,6 +208,7 @@ TRAFFIC_KERNELS = {
     "decode_paged_b64": ("decode", ["miattn_decode_split_kernel", "miattn_combine_kernel"]),
     "decode_long_ctx131072": ("long", ["miattn_decode_split_kernel", "miattn_combine_kernel"]),
     "chunked_prefill_8x1024": ("chunked", ["miattn_prefill_fwd_kernel"]),
+    "varlen_prefill_d256": ("varlen", ["miattn_prefill_fwd_kernel"]),
     "backward_causal_gqa_s4096": ("backward", ["miattn_bwd_prep_kernel", "miattn_bwd_dkdv_kernel",
                                                "miattn_bwd_dq_kernel"]),
 }
@@ -217,8 +218,8 @@ def summarize_counters(root: str):
     """Turn rocprofv3 --pmc runs into profiles/hbm_traffic.json.
 
     `root` holds one rocprofv3 output directory per (stage, counter), named
-    `<stage>_FETCH_SIZE` / `<stage>_WRITE_SIZE`, for the stages prefill, decode,
-    long and copy (the last from --only copy, a 1 GiB device copy). Counter
+    `<stage>_FETCH_SIZE` / `<stage>_WRITE_SIZE`, for every stage named in
+    TRAFFIC_KERNELS and for copy (--only copy, a 1 GiB device copy). Counter
     values are KiB per dispatch; each is scaled by (true bytes / counter
     bytes) of the copy, which reads and writes exactly 1 GiB."""
     import csv
@@ -281,7 +282,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = library policy")
     ap.add_argument("--long-splits", type=int, default=0, help="0 = library policy")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "chunked", "backward", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "chunked", "backward", "varlen", "copy"],
+                    default=None,
                     help="profiling aid: run just one stage (or a 1 GiB device copy used to calibrate "
                          "the HBM byte counters) for --steps iterations and print its mean time")
     ap.add_argument("--sweep-splits", action="store_true",
@@ -338,7 +340,7 @@ def main():
         return
 
     print("[bench] generating inputs", file=sys.stderr, flush=True)
-    want = {"prefill", "decode", "long", "chunked", "backward"} if args.only is None else {args.only}
+    want = {"prefill", "decode", "long", "chunked", "backward", "varlen"} if args.only is None else {args.only}
     P = Dd = Ld = None
     pc = synth.config2(S=4096, seed=0)
     if "prefill" in want or "backward" in want:
@@ -381,6 +383,16 @@ def main():
         mi.attn_fwd_paged(Cd["q"], Cd["kc"], Cd["vc"], Cd["bt"], Cd["cu"], Cd["sk"], cc.max_seqlen_q,
                           scale=cc.scale, causal=True, out=Cd["o"], lse=Cd["lse"])
 
+    vc5 = synth.config5(seed=0) if "varlen" in want else None
+    if vc5 is not None:
+        V5 = dict(q=bf16(vc5.q), k=bf16(vc5.k), v=bf16(vc5.v), cu=i32(vc5.cu_seqlens))
+        V5["o"] = torch.empty_like(V5["q"])
+        V5["lse"] = torch.empty((vc5.num_q_heads, vc5.total_tokens), dtype=torch.float32, device=dev)
+
+    def varlen():
+        mi.attn_fwd(V5["q"], V5["k"], V5["v"], V5["cu"], vc5.max_seqlen, scale=vc5.scale, causal=True,
+                    out=V5["o"], lse=V5["lse"])
+
     def backward():
         mi.attn_bwd(P["q"], P["k"], P["v"], P["o"], P["lse"], P["do"], P["cu"], pc.max_seqlen, scale=pc.scale,
                     causal=True, dq=P["dq"], dk=P["dk"], dv=P["dv"])
@@ -412,7 +424,7 @@ def main():
     stages = [prefill, decode, long_decode]
     if args.only is not None:
         f = {"prefill": prefill, "decode": decode, "long": long_decode, "chunked": chunked,
-             "backward": backward}[args.only]
+             "backward": backward, "varlen": varlen}[args.only]
         settle([f])
         for _ in range(args.warmup):
             f()
@@ -471,6 +483,19 @@ def main():
     be1.record(stream)
     torch.cuda.synchronize()
     t_bwd = be0.elapsed_time(be1) / args.steps * 1e-3
+    # varlen packed causal prefill at head_dim 256 (beside the step as well)
+    for _ in range(args.warmup):
+        varlen()
+    ve0 = torch.cuda.Event(enable_timing=True)
+    ve1 = torch.cuda.Event(enable_timing=True)
+    ve0.record(stream)
+    for _ in range(args.steps):
+        varlen()
+    ve1.record(stream)
+    torch.cuda.synchronize()
+    t_var = ve0.elapsed_time(ve1) / args.steps * 1e-3
+    fl_var = accounting.prefill_flops(vc5.seqlens, vc5.num_q_heads, vc5.head_dim, True)
+    by_var = accounting.prefill_bytes(vc5.total_tokens, vc5.num_q_heads, vc5.num_kv_heads, vc5.head_dim)
     fl_bwd = accounting.backward_flops(pc.seqlens, pc.num_q_heads, pc.head_dim, True)
     by_bwd = accounting.backward_bytes(pc.total_tokens, pc.num_q_heads, pc.num_kv_heads, pc.head_dim)
 
@@ -533,11 +558,19 @@ def main():
                          "traffic": traffic_from_profile("backward_causal_gqa_s4096", by_bwd),
                          "work": "5 products per admissible pair (2.5x the forward)",
                          "timing": "its own loop of --steps calls after the step loop"},
+            "varlen_prefill_d256": {"seqlens": [int(x) for x in vc5.seqlens], "Hq": 16, "Hkv": 4, "D": 256,
+                                    "causal": True, "ms": round(t_var * 1e3, 4),
+                                    "TFLOP/s": round(fl_var / t_var / 1e12, 2),
+                                    "frac_mfma": round(fl_var / t_var / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                    "algorithmic_gflop": round(fl_var / 1e9, 3),
+                                    "algorithmic_MB": round(by_var / 1e6, 2),
+                                    "traffic": traffic_from_profile("varlen_prefill_d256", by_var),
+                                    "timing": "its own loop of --steps calls after the step loop"},
             "wall_s": round(wall, 4),
         },
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
-                     "kernel": "miattn_prefill_pp_kernel<128, true>",
+                     "kernel": "miattn_prefill_pp_kernel<128, 2, true>",
                      "per_launch_work": f"{fl_pre:.6g} FLOP"},
         "roofline_decode": {"bound": "hbm", "achieved": round(gbs_long, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(gbs_long / PEAK_HBM_GBS, 4),
