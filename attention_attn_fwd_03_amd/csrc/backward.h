@@ -64,6 +64,8 @@ struct BwdArgs {
   int group;                  // G
   int heads_per_wg;           // dQ kernel: query heads per workgroup (NH)
   int n_head_slots;           // dQ kernel: Hkv * G / NH
+  int n_kblocks;              // dK/dV grid: 32-key blocks per sequence (ceil(max_seqlen / 32))
+  int n_qunits;               // dQ grid: query tiles per sequence
   float c;                    // scale * log2(e)
   float scale;
 };
@@ -155,13 +157,14 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float st_lds1[4 * 64];
   __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[2 * TILE];   // the 32 keys' K, then V
 
-  // work item: (kv head, key block, sequence), kv head fastest; key block 0
-  // (the most causal work) first
+  // work item: (kv head, key block, sequence), kv head fastest, sequence
+  // slowest (the workgroups resident together read one sequence's Q/dO, which
+  // then stays in L2); key block 0 (the most causal work) first
   const int lin = blockIdx.x;
   const int g = lin % a.num_kv_heads;
   const int rest = lin / a.num_kv_heads;
-  const int kblk = rest / a.num_seqs;
-  const int b = rest % a.num_seqs;
+  const int kblk = rest % a.n_kblocks;
+  const int b = rest / a.n_kblocks;
   int s0 = a.cu_seqlens[b];
   int s1 = a.cu_seqlens[b + 1];
   s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
@@ -452,13 +455,14 @@ __global__ __launch_bounds__(256, 2) void miattn_bwd_dq_kernel(BwdArgs a) {
   const int WQ = 4 / NH;
   const int QR = 32 * WQ;
 
-  // work item: (head slot, query tile, sequence), head slot fastest; the last
-  // query tiles (the most causal work) first
+  // work item: (head slot, query tile, sequence), head slot fastest, sequence
+  // slowest (one sequence's K/V stays in L2); the last query tiles (the most
+  // causal work) first
   const int lin = blockIdx.x;
   const int hslot = lin % a.n_head_slots;
   const int rest = lin / a.n_head_slots;
-  const int b = rest % a.num_seqs;
-  const int unit = rest / a.num_seqs;
+  const int unit = rest % a.n_qunits;
+  const int b = rest / a.n_qunits;
   int s0 = a.cu_seqlens[b];
   int s1 = a.cu_seqlens[b + 1];
   s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);

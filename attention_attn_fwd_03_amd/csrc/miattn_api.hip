@@ -581,9 +581,11 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
   const long rows = (long)total_tokens * (num_q_heads + num_kv_heads);
   const int rpb = 256 / (head_dim / 8);
   const unsigned g_prep = (unsigned)((rows + rpb - 1) / rpb);
-  const unsigned g_dkdv = (unsigned)((long)num_kv_heads * ((max_seqlen + 31) / 32) * num_seqs);
+  a.n_kblocks = (max_seqlen + 31) / 32;
+  const unsigned g_dkdv = (unsigned)((long)num_kv_heads * a.n_kblocks * num_seqs);
   const int QR = 32 * (4 / a.heads_per_wg);
-  const unsigned g_dq = (unsigned)((long)a.n_head_slots * ((max_seqlen + QR - 1) / QR) * num_seqs);
+  a.n_qunits = (max_seqlen + QR - 1) / QR;
+  const unsigned g_dq = (unsigned)((long)a.n_head_slots * a.n_qunits * num_seqs);
   const dim3 blk(256);
   if (head_dim == 64) {
     hipLaunchKernelGGL(miattn::miattn_bwd_prep_kernel<64>, dim3(g_prep), blk, 0, st, a);
