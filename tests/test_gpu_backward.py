@@ -137,3 +137,16 @@ def test_repeatable_bitwise():
     b = gpu_pipeline(c, dout)
     for x, y in zip(a, b):
         assert bitwise_equal(x, y)
+
+
+def test_max_seqlen_overestimate_gives_same_bits():
+    c = synth.make_prefill(9, 8, [300, 77, 1000, 1], 8, 2, 128, 0.088, True, "bf16", "bwd_overestimate")
+    dout = synth.output_gradient(9, 8, c.total_tokens, c.num_q_heads, c.head_dim)
+    q, k, v, cu = bf16_dev(c.q), bf16_dev(c.k), bf16_dev(c.v), i32_dev(c.cu_seqlens)
+    o, lse = mi.attn_fwd(q, k, v, cu, max_len(c), scale=c.scale, causal=True)
+    do = bf16_dev(dout)
+    a = mi.attn_bwd(q, k, v, o, lse, do, cu, max_len(c), scale=c.scale, causal=True)
+    b = mi.attn_bwd(q, k, v, o, lse, do, cu, 3 * max_len(c) + 5, scale=c.scale, causal=True)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert bitwise_equal(x, y)

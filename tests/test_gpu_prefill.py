@@ -147,3 +147,16 @@ def test_score_shift_moves_lse_only():
     o1, l1 = run(c1)
     assert_bf16_close(host(o1), host(o0), "shifted vs unshifted")
     assert np.max(np.abs(host(l1) - (host(l0) + 0.5))) <= 1e-3
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_max_seqlen_overestimate_gives_same_bits(D):
+    # a larger max_seqlen only adds workgroups that exit at once; the
+    # sequence-major grid must still map every (sequence, tile pair) the same
+    case = synth.make_prefill(24, D, [300, 77, 1000, 1], 8, 2, D, 1 / math.sqrt(D), True, "bf16",
+                              f"overestimate_d{D}")
+    q, k, v, cu = bf16_dev(case.q), bf16_dev(case.k), bf16_dev(case.v), i32_dev(case.cu_seqlens)
+    o1, l1 = mi.attn_fwd(q, k, v, cu, case.max_seqlen, scale=case.scale, causal=True)
+    o2, l2 = mi.attn_fwd(q, k, v, cu, 3 * case.max_seqlen + 5, scale=case.scale, causal=True)
+    torch.cuda.synchronize()
+    assert bitwise_equal(o1, o2) and bitwise_equal(l1, l2)

@@ -105,3 +105,13 @@ def test_repeatable_bitwise():
     o1, l1 = run(c)
     o2, l2 = run(c)
     assert bitwise_equal(o1, o2) and bitwise_equal(l1, l2)
+
+
+def test_max_seqlen_overestimate_gives_same_bits():
+    c = synth.make_chunked_prefill(6, 5, [200, 1, 64], [900, 1, 64], 8, 2, 128, 0.088, shuffle=True, tail="zero")
+    args = (bf16_dev(c.q), bf16_dev(c.k_cache), bf16_dev(c.v_cache), i32_dev(c.block_table),
+            i32_dev(c.cu_seqlens_q), i32_dev(c.seq_lens_k))
+    o1, l1 = mi.attn_fwd_paged(*args, c.max_seqlen_q, scale=c.scale, causal=True)
+    o2, l2 = mi.attn_fwd_paged(*args, 4 * c.max_seqlen_q + 3, scale=c.scale, causal=True)
+    torch.cuda.synchronize()
+    assert bitwise_equal(o1, o2) and bitwise_equal(l1, l2)
