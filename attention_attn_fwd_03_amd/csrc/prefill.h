@@ -344,7 +344,11 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
             m[qb] = mn;
           }
         }
-        // P = exp2(s c - m), rounded to bf16 for P.V; l sums the fp32 values
+        // P = exp2(s c - m), rounded to bf16 for P.V; the tile's row sum ls
+        // adds the fp32 values in score order, then l += ls
+        float ls[QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) ls[qb] = 0.f;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
           u32x4 pw[QB][2];
@@ -355,7 +359,7 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
             for (int r = 0; r < 16; r += 2) {
               const float p0 = exp2_hw(__builtin_fmaf(s[qb][kb][r], c, nmu));
               const float p1 = exp2_hw(__builtin_fmaf(s[qb][kb][r + 1], c, nmu));
-              l[qb] += p0 + p1;
+              ls[qb] += p0 + p1;
               pw[qb][r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
             }
           }
@@ -380,6 +384,8 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
             }
           }
         }
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) l[qb] += ls[qb];
       }
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // tile kt+1 has landed in LDS
       __syncthreads();

@@ -24,8 +24,10 @@
 // Lanes, swizzles and MFMA shapes follow the four-wave kernel: S^T = K Q^T on
 // 32x32x16 bf16 MFMAs (lane l owns query row l % 32, 16 of every 32 keys),
 // V^T through ds_read_b64_tr_b16, the lazy running max (moves only when a
-// tile's max exceeds it by more than 2^8). Tiles, accumulation orders and the
-// softmax rule are the four-wave kernel's, so both give the same bits.
+// tile's max exceeds it by more than 2^8; the tile max is taken only when the
+// tile's probabilities against the current max could reach that). Tiles,
+// accumulation orders and the softmax rule are the four-wave kernel's, so
+// both give the same bits.
 #pragma once
 
 #include "prefill.h"
@@ -226,7 +228,7 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
         pp_mfma_reads<NKK * KB, 1, 4>();
       }
     };
-    // SOFT(t): mask, max, lazy rescale, P(t) = exp2(s c - m) in bf16
+    // SOFT(t): mask, lazy rescale, P(t) = exp2(s c - m) in bf16
     auto soft = [&](int t) __attribute__((always_inline)) {
       if (t >= n_kt_w) return;
       const bool need_mask = (t + 1) * BC > Lk || (CAUSAL && (t + 1) * BC - 1 > q0 + off);
@@ -246,34 +248,55 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
           for (int r = 0; r < 16; ++r)
             s[kb][r] = (32 * kb + 8 * (r >> 2) + (r & 3)) < lim ? s[kb][r] : kNegInf;
       }
-      // row max of the tile; the running max moves only when it exceeds it
-      // by more than 2^8 (as in the four-wave kernel, whose bits this kernel
-      // reproduces)
-      float smax = kNegInf;
+      // P(t) = exp2(s c - m) in bf16 and the tile's row sum ls (fp32 values,
+      // summed in score order, then added to l)
+      auto exps = [&](float nmu) __attribute__((always_inline)) {
+        float ls = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) smax = fmaxf(smax, s[kb][r]);
-      smax = fmaxf(smax, xor32(smax));
-      const float tmax = smax * c;   // scale > 0, so max(s c) = c max(s)
-      if (__builtin_amdgcn_ballot_w64(tmax > m + kFwdRescaleThreshold)) {
-        const float mn = fmaxf(m, tmax);
-        const float alpha = (m == kNegInf) ? 0.f : exp2_hw(m - mn);
-        l *= alpha;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
-        m = mn;
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, nmu));
+            const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, nmu));
+            ls += p0 + p1;
+            pw[kb][r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
+          }
+        return ls;
+      };
+      // The running max moves only when the tile's max exceeds it by more
+      // than 2^8 (the four-wave kernel's rule, whose bits this kernel
+      // reproduces). That needs the tile max only when some probability
+      // taken against the current max could exceed 2^8: with a finite max in
+      // every lane and every lane's sum at most 2^6, no score is within 2
+      // (log2 units) of the threshold, so the rule keeps the max and the
+      // probabilities already computed are the ones it would give. Otherwise
+      // (the first tile, a large or non-finite sum) take the max and apply
+      // the rule, then recompute.
+      bool slow = __builtin_amdgcn_ballot_w64(m == kNegInf) != 0;
+      float ls = 0.f;
+      if (!slow) {
+        ls = exps(-m);
+        slow = __builtin_amdgcn_ballot_w64(!(ls <= 64.f)) != 0;
       }
-      const float nmu = (m == kNegInf) ? 0.f : -m;
+      if (slow) {
+        float smax = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, nmu));
-          const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, nmu));
-          l += p0 + p1;
-          pw[kb][r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
+          for (int r = 0; r < 16; ++r) smax = fmaxf(smax, s[kb][r]);
+        smax = fmaxf(smax, xor32(smax));
+        const float tmax = smax * c;   // scale > 0, so max(s c) = c max(s)
+        if (__builtin_amdgcn_ballot_w64(tmax > m + kFwdRescaleThreshold)) {
+          const float mn = fmaxf(m, tmax);
+          const float alpha = (m == kNegInf) ? 0.f : exp2_hw(m - mn);
+          l *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+          m = mn;
         }
+        ls = exps((m == kNegInf) ? 0.f : -m);
+      }
+      l += ls;
     };
 
     // Global phases 0 .. 2 n_kt + 1, a barrier after each. Group 0 runs
