@@ -320,49 +320,75 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
                 s[qb][kb][r] = (32 * kb + 8 * (r >> 2) + (r & 3)) < lim ? s[qb][kb][r] : kNegInf;
           }
         }
-        float tmax[QB];
-        bool grow = false;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          float smax = kNegInf;
-#pragma unroll
-          for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) smax = fmaxf(smax, s[qb][kb][r]);
-          smax = fmaxf(smax, xor32(smax));
-          tmax[qb] = smax * c;   // scale > 0, so max(s c) = c max(s)
-          grow = grow || (tmax[qb] > m[qb] + kFwdRescaleThreshold);
-        }
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const float mn = fmaxf(m[qb], tmax[qb]);
-            const float alpha = (m[qb] == kNegInf) ? 0.f : exp2_hw(m[qb] - mn);
-            l[qb] *= alpha;
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) acc[qb][dt] *= alpha;
-            m[qb] = mn;
-          }
-        }
         // P = exp2(s c - m), rounded to bf16 for P.V; the tile's row sum ls
         // adds the fp32 values in score order, then l += ls
+        u32x4 pw[QB][KB][2];
         float ls[QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) ls[qb] = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          u32x4 pw[QB][2];
+        auto exps = [&]() __attribute__((always_inline)) {
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             const float nmu = (m[qb] == kNegInf) ? 0.f : -m[qb];
+            ls[qb] = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
-              const float p0 = exp2_hw(__builtin_fmaf(s[qb][kb][r], c, nmu));
-              const float p1 = exp2_hw(__builtin_fmaf(s[qb][kb][r + 1], c, nmu));
-              ls[qb] += p0 + p1;
-              pw[qb][r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; r += 2) {
+                const float p0 = exp2_hw(__builtin_fmaf(s[qb][kb][r], c, nmu));
+                const float p1 = exp2_hw(__builtin_fmaf(s[qb][kb][r + 1], c, nmu));
+                ls[qb] += p0 + p1;
+                pw[qb][kb][r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
+              }
+          }
+        };
+        // lazy rescale: the running max moves only when the tile's max
+        // exceeds it by more than 2^8. The tile max is needed only when a
+        // probability against the current max could reach that: with a finite
+        // max in every lane and every lane's sum at most 2^6, no score is
+        // within 2 (log2 units) of the threshold and the probabilities
+        // already computed stand. Otherwise (first tile, large or non-finite
+        // sums) take the max, apply the rule and recompute
+        // (32-key tiles hold too few scores per lane for the check to pay:
+        // they always take the max)
+        bool unset = false;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) unset = unset || m[qb] == kNegInf;
+        bool slow = KB < 2 || __builtin_amdgcn_ballot_w64(unset) != 0;
+        if (!slow) {
+          exps();
+          bool big = false;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) big = big || !(ls[qb] <= 64.f);
+          slow = __builtin_amdgcn_ballot_w64(big) != 0;
+        }
+        if (slow) {
+          float tmax[QB];
+          bool grow = false;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            float smax = kNegInf;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) smax = fmaxf(smax, s[qb][kb][r]);
+            smax = fmaxf(smax, xor32(smax));
+            tmax[qb] = smax * c;   // scale > 0, so max(s c) = c max(s)
+            grow = grow || (tmax[qb] > m[qb] + kFwdRescaleThreshold);
+          }
+          if (__builtin_amdgcn_ballot_w64(grow)) {
+#pragma unroll
+            for (int qb = 0; qb < QB; ++qb) {
+              const float mn = fmaxf(m[qb], tmax[qb]);
+              const float alpha = (m[qb] == kNegInf) ? 0.f : exp2_hw(m[qb] - mn);
+              l[qb] *= alpha;
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) acc[qb][dt] *= alpha;
+              m[qb] = mn;
             }
           }
+          exps();
+        }
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
           // O^T += V^T P^T; V^T rows via the transposing read: block bb of
           // 16 lanes reads keys 32kb + 16u + 4(bb/2) + {0..3} (+8), columns
           // 32 dt + 16 (bb%2) + {0..15}
@@ -379,7 +405,7 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
               const bf16x8 vop = as_bf16x8(lo, hi);
 #pragma unroll
               for (int qb = 0; qb < QB; ++qb) {
-                acc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, as_bf16x8(pw[qb][u]), acc[qb][dt], 0, 0, 0);
+                acc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, as_bf16x8(pw[qb][kb][u]), acc[qb][dt], 0, 0, 0);
               }
             }
           }
