@@ -160,3 +160,28 @@ def test_max_seqlen_overestimate_gives_same_bits(D):
     o2, l2 = mi.attn_fwd(q, k, v, cu, 3 * case.max_seqlen + 5, scale=case.scale, causal=True)
     torch.cuda.synchronize()
     assert bitwise_equal(o1, o2) and bitwise_equal(l1, l2)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_rising_scores_take_every_softmax_path(D, causal):
+    # channel 0 (q = 1, k = r_j) adds scale * r_j to key j's score, r rising
+    # along the keys: about 0.1 log2 units per key at kv head 0 and 0.6 at
+    # head 1. Later tiles then stay within 2^8 of the running max (kept),
+    # pass it (rescaled), or have tile sums above 2^6 while staying below it
+    # (the max is taken and the rule keeps it); head 1 rises by ~600 log2
+    # units over 1000 keys, which overflows fp32 unless every rescale happens
+    case = synth.make_prefill(25, D, [1000, 333], 4, 2, D, 1 / math.sqrt(D), causal, "bf16", f"ramp_d{D}")
+    c = case.scale * math.log2(math.e)
+    for b in range(2):
+        s0, s1 = int(case.cu_seqlens[b]), int(case.cu_seqlens[b + 1])
+        j = np.arange(s1 - s0, dtype=np.float64)
+        for h, slope in enumerate((0.1, 0.6)):
+            case.k[s0:s1, h, 0] = synth.bf16_bits((slope / c * j).astype(np.float32))
+    case.q[:, :, 0] = synth.bf16_bits(np.float32(1.0))
+    # the ramp makes the attention peaky (O copies single V rows); V / 4
+    # (exact in bf16) keeps |O| below 1, where bf16 output rounding stays
+    # far inside the bar
+    case.v[:] = synth.bf16_bits((synth.bf16_to_f64(case.v) / 4).astype(np.float32))
+    o, l = full_check(case)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()

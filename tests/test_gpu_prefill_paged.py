@@ -1,6 +1,8 @@
 """Chunked prefill against a paged cache: the HIP kernel against the fp64
 oracle (bf16: max-abs 1e-2, mean-abs 1e-3; LSE: 1e-3), plus the properties
 that tie it to the contiguous prefill."""
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -115,3 +117,25 @@ def test_max_seqlen_overestimate_gives_same_bits():
     o2, l2 = mi.attn_fwd_paged(*args, 4 * c.max_seqlen_q + 3, scale=c.scale, causal=True)
     torch.cuda.synchronize()
     assert bitwise_equal(o1, o2) and bitwise_equal(l1, l2)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_rising_scores_take_every_softmax_path(D):
+    # channel 0 (q = 1, k = r_p) adds scale * r_p to the score of cached key
+    # p, rising ~0.1 (kv head 0) and ~0.6 (head 1) log2 units per key: tiles
+    # kept, rescaled, and above the tile-sum bound without a rescale; head 1
+    # rises by ~600 log2 units over 1000 keys (fp32 overflow without every
+    # rescale)
+    c = synth.make_chunked_prefill(6, 40 + D, [300, 64], [1000, 700], 4, 2, D, D ** -0.5, shuffle=True,
+                                   tail="zero")
+    cl = c.scale * math.log2(math.e)
+    for b, L in enumerate(c.seq_lens_k.tolist()):
+        pos = np.arange(L)
+        pages, slots = c.block_table[b, pos // 16], pos % 16
+        for h, slope in enumerate((0.1, 0.6)):
+            c.k_cache[pages, slots, h, 0] = synth.bf16_bits((slope / cl * pos).astype(np.float32))
+    c.q[:, :, 0] = synth.bf16_bits(np.float32(1.0))
+    # peaky attention copies single V rows: V / 4 (exact) keeps |O| below 1
+    c.v_cache[:] = synth.bf16_bits((synth.bf16_to_f64(c.v_cache) / 4).astype(np.float32))
+    o, l = check(c, True)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(l).all()
