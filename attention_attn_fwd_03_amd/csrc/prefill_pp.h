@@ -19,7 +19,10 @@
 // copies of K(u + 1) and V(u) into the buffers that K(u - 1) and V(u - 2)
 // held (their last readers finished in phase 2u - 1); every wave waits for
 // its share at the end of phase 2u + 1, before the barrier, so both tiles are
-// in LDS when phase 2u + 2 reads them. Two buffers each for K and V.
+// in LDS when phase 2u + 2 reads them. Two buffers each for K and V. A
+// workgroup takes two query tiles in turn; the second tile's Q rows are
+// loaded in the first one's last step (its last S is done, no copy is in
+// flight), so their latency hides behind the last P V and the epilogue.
 //
 // Lanes, swizzles and MFMA shapes follow the four-wave kernel: S^T = K Q^T on
 // 32x32x16 bf16 MFMAs (lane l owns query row l % 32, 16 of every 32 keys),
@@ -157,21 +160,25 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
   const uint32_t v_lane = (uint32_t)(rl * (2 * D) + 16 * c0 + 8 * (kq & 1));
   const uint32_t v_x = (uint32_t)((TL::vswz(rl) >> 2) << 6);
 
-  for (int tsel = 0; tsel < n_mine; ++tsel) {
-    const int qt = tsel == 0 ? pair : n_tiles - 1 - pair;
-    const int q0 = qt * QR + 32 * (grp * WQ + qs);   // first query row of this wave
-
-    u32x4 qop[NKK];
-    {
-      const int row = q0 + (lane & 31);
-      const bool ok = row < Lq;
-      const uint16_t* qp = a.q + ((size_t)(s0 + (ok ? row : 0)) * Hq + h) * D + 8 * half;
+  auto tile_of = [&](int ts) { return ts == 0 ? pair : n_tiles - 1 - pair; };
+  // Q rows of this wave for query tile qt, straight into B-operand registers
+  // (rows past the last query as zeros)
+  u32x4 qop[NKK];
+  auto load_q = [&](int qt) __attribute__((always_inline)) {
+    const int row = qt * QR + 32 * (grp * WQ + qs) + (lane & 31);
+    const bool ok = row < Lq;
+    const uint16_t* qp = a.q + ((size_t)(s0 + (ok ? row : 0)) * Hq + h) * D + 8 * half;
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        qop[kk] = ok ? ld16(qp + 16 * kk) : z;
-      }
+    for (int kk = 0; kk < NKK; ++kk) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qop[kk] = ok ? ld16(qp + 16 * kk) : z;
     }
+  };
+  load_q(tile_of(0));
+
+  for (int tsel = 0; tsel < n_mine; ++tsel) {
+    const int qt = tile_of(tsel);
+    const int q0 = qt * QR + 32 * (grp * WQ + qs);   // first query row of this wave
 
     auto clampk = [&](int x) { return x < 0 ? 0 : (x > Lk ? Lk : x); };
     const int kend_wg = CAUSAL ? clampk(qt * QR + QR + off) : Lk;
@@ -313,14 +320,19 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
       copies(0);
       __syncthreads();
     }
+    // In the last step (i = n_kt) no copy is in flight and Q is dead (the
+    // last S was in step n_kt - 1): the next query tile's Q rows are loaded
+    // there and travel through the last P V and the epilogue; the next
+    // pass's first wait covers them.
     for (int i = 0; i <= n_kt; ++i) {
+      if (i == n_kt && tsel + 1 < n_mine) load_q(tile_of(tsel + 1));
       gemm(i);
       if (grp == 0) copies(i);
-      if (grp == 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (grp == 1 && i < n_kt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (i < n_kt) soft(i);
       if (grp == 1 && i + 1 <= n_kt) copies(i + 1);
-      if (grp == 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (grp == 0 && i < n_kt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       if (grp == 0 || i < n_kt) __syncthreads();
     }
 
