@@ -23,6 +23,9 @@
 // workgroup takes two query tiles in turn; the second tile's Q rows are
 // loaded in the first one's last step (its last S is done, no copy is in
 // flight), so their latency hides behind the last P V and the epilogue.
+// The epilogue stages each wave's normalised output in the (then free) K/V
+// buffers and writes whole rows, 16 bytes per lane: a direct store from the
+// accumulator layout would write 8 bytes into each of 32 rows per instruction.
 //
 // Lanes, swizzles and MFMA shapes follow the four-wave kernel: S^T = K Q^T on
 // 32x32x16 bf16 MFMAs (lane l owns query row l % 32, 16 of every 32 keys),
@@ -337,12 +340,20 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
     }
 
     // --- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 --------------------
+    // After the loop's last barrier the K/V buffers are free: each wave stages
+    // its 32 x D block of O there (bf16, chunk c of row r in slot c ^ (r mod
+    // CH, at most 16)), then stores whole rows, 16 bytes per lane.
     const float lt = l + xor32(l);
     const int qrow = q0 + (lane & 31);
-    if (qrow < Lq) {
-      const bool empty = !(lt > 0.f);
-      const float inv = empty ? 0.f : 1.f / lt;
-      uint16_t* op = a.o + ((size_t)(s0 + qrow) * Hq + h) * D + 4 * half;
+    const bool empty = !(lt > 0.f);
+    const float inv = empty ? 0.f : 1.f / lt;
+    constexpr int OB = 32 * D * 2;   // bytes of one wave's block
+    static_assert(2 * OB <= TL::TILE_BYTES, "two waves' blocks per K/V buffer");
+    auto osw = [&](int r) { return r & (CH >= 16 ? 15 : CH - 1); };
+    MIATTN_LDS uint8_t* stg = ((wave >> 2) ? vbuf((wave >> 1) & 1) : kbuf((wave >> 1) & 1)) + (wave & 1) * OB;
+    {
+      const int r = lane & 31;
+      MIATTN_LDS uint8_t* sr = stg + r * (2 * D) + 8 * half;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -350,11 +361,22 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
           const f32x16& A = acc[dt];
           u32x2 w = {pack_bf16x2(A[4 * r4] * inv, A[4 * r4 + 1] * inv),
                      pack_bf16x2(A[4 * r4 + 2] * inv, A[4 * r4 + 3] * inv)};
-          *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * r4) = w;
+          *reinterpret_cast<MIATTN_LDS u32x2*>(sr + 16 * ((4 * dt + r4) ^ osw(r))) = w;
         }
-      if (a.lse != nullptr && half == 0)
-        a.lse[(size_t)h * a.total_tokens + s0 + qrow] = empty ? kNegInf : (m + log2_hw(lt)) * kLn2;
     }
+    // the lane index from an opaque instruction, so that the store addresses
+    // are formed here rather than held through the loop
+    int ln;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+#pragma unroll
+    for (int j = 0; j < 32 * CH / 64; ++j) {
+      const int lidx = 64 * j + ln;
+      const int r = lidx / CH, ch = lidx % CH;
+      const u32x4 w = lds_ld16(stg + r * (2 * D) + 16 * (ch ^ osw(r)));
+      if (q0 + r < Lq) st16(a.o + ((size_t)(s0 + q0 + r) * Hq + h) * D + 8 * ch, w);
+    }
+    if (qrow < Lq && a.lse != nullptr && half == 0)
+      a.lse[(size_t)h * a.total_tokens + s0 + qrow] = empty ? kNegInf : (m + log2_hw(lt)) * kLn2;
   }
 }
 
