@@ -1,4 +1,5 @@
-// Tiled prefill forward, ping-pong form (dense K/V, head_dim 64 and 128).
+// Tiled prefill forward, ping-pong form (dense K/V, head_dim 64 and 128;
+// causal, and non-causal as the causal code with every key visible).
 //
 // The same computation as miattn_prefill_fwd_kernel (the FlashAttention
 // forward of "Streaming process", steps 3-8: S = Q K^T per K/V tile, online
@@ -88,7 +89,10 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
   s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
   const int Lq = s1 - s0;
   const int Lk = Lq;
-  const int off = 0;   // causal: query i sees keys j <= i
+  // causal: query i sees keys j <= i + off; off = Lk (see_all) makes every
+  // key visible, so the non-causal case runs this same code and only the
+  // tail tile is masked
+  const int off = a.see_all ? Lk : 0;
   const int n_tiles = (Lq + QR - 1) / QR;
   // query tiles i and n-1-i together cost the same for every pair (causal)
   if (pair > n_tiles - 1 - pair) return;   // uniform over the workgroup
