@@ -96,10 +96,10 @@ constexpr bool fwd_pingpong(int d, bool paged) { return d <= 128 && !paged; }
 
 template <int D, int KB>
 void launch_fwd_pp(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t st) {
-  // one instantiation: non-causal is the causal code with every key visible
-  miattn::FwdArgs b = a;
-  b.see_all = causal ? 0 : 1;
-  hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, KB, true>), dim3(grid), dim3(512), 0, st, b);
+  if (causal)
+    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, KB, true>), dim3(grid), dim3(512), 0, st, a);
+  else
+    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, KB, false>), dim3(grid), dim3(512), 0, st, a);
 }
 
 // bf16 prefill grid: (head slot, query-tile pair, sequence)
@@ -107,7 +107,6 @@ long fwd_setup(miattn::FwdArgs& a, int num_seqs, int max_seqlen, int num_q_heads
                bool unit_per_tile = false) {
   const int G = num_q_heads / num_kv_heads;
   a.num_seqs = num_seqs;
-  a.see_all = 0;
   a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
   a.heads_per_wg = G >= 4 ? 4 : G;
   const int QR = 32 * fwd_qb(head_dim) * (4 / a.heads_per_wg) * (fwd_pingpong(head_dim, unit_per_tile) ? 2 : 1);

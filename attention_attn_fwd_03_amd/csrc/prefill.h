@@ -64,9 +64,6 @@ struct FwdArgs {
   const int32_t* block_table; // [num_seqs, max_pages]
   int max_pages;
   int num_pages;
-  // dense ping-pong kernel: every query sees every key (the non-causal case
-  // runs the causal code with the diagonal moved past the last key)
-  int see_all;
 };
 
 constexpr float kFwdRescaleThreshold = 8.0f;

@@ -89,10 +89,16 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
   s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
   const int Lq = s1 - s0;
   const int Lk = Lq;
-  // causal: query i sees keys j <= i + off; off = Lk (see_all) makes every
-  // key visible, so the non-causal case runs this same code and only the
-  // tail tile is masked
-  const int off = a.see_all ? Lk : 0;
+  // query i sees keys j <= i + off: 0 for causal; Lk (every key visible)
+  // for non-causal, which then runs the same code with only the tail tile
+  // masked. The non-causal value is made opaque to the compiler: folded into
+  // a separate non-causal form, the kernel ran short of scalar registers and
+  // lost its operand prefetch.
+  int off = 0;
+  if (!CAUSAL) {
+    off = Lk;
+    asm volatile("" : "+s"(off));
+  }
   const int n_tiles = (Lq + QR - 1) / QR;
   // query tiles i and n-1-i together cost the same for every pair (causal)
   if (pair > n_tiles - 1 - pair) return;   // uniform over the workgroup
@@ -188,9 +194,9 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
     const int q0 = qt * QR + 32 * (grp * WQ + qs);   // first query row of this wave
 
     auto clampk = [&](int x) { return x < 0 ? 0 : (x > Lk ? Lk : x); };
-    const int kend_wg = CAUSAL ? clampk(qt * QR + QR + off) : Lk;
+    const int kend_wg = clampk(qt * QR + QR + off);
     const int n_kt = (kend_wg + BC - 1) / BC;   // tiles of the workgroup
-    const int kend_w = CAUSAL ? clampk(q0 + 32 + off) : Lk;
+    const int kend_w = clampk(q0 + 32 + off);
     const int n_kt_w = q0 < Lq ? (kend_w + BC - 1) / BC : 0;   // tiles this wave computes
 
     float m = kNegInf, l = 0.f;
@@ -245,17 +251,15 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
     // SOFT(t): mask, lazy rescale, P(t) = exp2(s c - m) in bf16
     auto soft = [&](int t) __attribute__((always_inline)) {
       if (t >= n_kt_w) return;
-      const bool need_mask = (t + 1) * BC > Lk || (CAUSAL && (t + 1) * BC - 1 > q0 + off);
+      const bool need_mask = (t + 1) * BC > Lk || (t + 1) * BC - 1 > q0 + off;
       if (need_mask) {
         // key of score r in block kb: t BC + 4 half + (32 kb + 8 (r / 4) + r % 4);
         // it is kept iff that offset is below lim (one compare with an
         // immediate per score, no per-score registers)
         const int kbase_lane = t * BC + 4 * half;
         int lim = Lk - kbase_lane;
-        if (CAUSAL) {
-          const int lc = q0 + (lane & 31) + off + 1 - kbase_lane;
-          lim = lc < lim ? lc : lim;
-        }
+        const int lc = q0 + (lane & 31) + off + 1 - kbase_lane;
+        lim = lc < lim ? lc : lim;
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
