@@ -96,6 +96,9 @@ def test_varlen_d256_full_size_sampled():
     ([300], 4, 4, 128, True),
     ([333, 64], 32, 8, 128, False),  # G = 4 non-causal, ragged
     ([100, 257], 8, 4, 64, False),   # G = 2, D = 64 non-causal
+    ([1000, 513], 8, 8, 128, True),  # G = 1: 256-row tiles, two-pass and single (middle) work items
+    ([700, 3], 8, 4, 128, False),    # G = 2 non-causal, two passes and a ragged tail
+    ([600, 5], 16, 2, 128, False),   # G = 8 non-causal
 ])
 def test_shapes(lens, Hq, Hkv, D, causal):
     full_check(synth.make_prefill(20, 0, lens, Hq, Hkv, D, 1 / math.sqrt(D), causal, "bf16",
