@@ -100,6 +100,14 @@ def _stream(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
+def _check_decode_tables(block_table, seq_lens, batch: int):
+    # the kernels read block_table[b, :] and seq_lens[b] for every b < batch
+    if block_table.dim() != 2 or block_table.shape[0] != batch or block_table.shape[1] < 1:
+        raise ValueError(f"block_table must be [batch={batch}, max_pages >= 1], got {tuple(block_table.shape)}")
+    if seq_lens.dim() != 1 or seq_lens.numel() != batch:
+        raise ValueError(f"seq_lens must be [batch={batch}], got {tuple(seq_lens.shape)}")
+
+
 def _need_cuda(*ts):
     for t in ts:
         if t is not None and (not t.is_cuda or not t.is_contiguous()):
@@ -214,7 +222,6 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
     """Paged split-KV decode. q [B,Hq,D] bf16; caches [pages,16,Hkv,D] bf16;
     block_table int32 [B,max_pages]; seq_lens int32 [B]. Returns
     (o [B,Hq,D] bf16, lse [B,Hq] fp32)."""
-    _need_cuda(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
     B, Hq, D = q.shape
     num_pages, page, Hkv, Dk = k_cache.shape
     if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
@@ -223,6 +230,8 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
         raise ValueError("cache shapes do not match q")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_table and seq_lens must be int32")
+    _check_decode_tables(block_table, seq_lens, B)
+    _need_cuda(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
     o = out if out is not None else torch.empty_like(q)
     if return_lse and lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
@@ -253,7 +262,6 @@ def attn_decode_paged_numerics(q, k_cache, v_cache, block_table, seq_lens, *, sc
     """Paged split-KV decode with selectable split records, rounding points
     and group geometry (see miattn_attn_decode_paged_numerics). Same inputs as
     attn_decode_paged; returns (o [B,Hq,D] of out_dtype, lse [B,Hq] fp32)."""
-    _need_cuda(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
     B, Hq, D = q.shape
     num_pages, page, Hkv, Dk = k_cache.shape
     if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
@@ -262,6 +270,8 @@ def attn_decode_paged_numerics(q, k_cache, v_cache, block_table, seq_lens, *, sc
         raise ValueError("cache shapes do not match q")
     if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
         raise ValueError("block_table and seq_lens must be int32")
+    _check_decode_tables(block_table, seq_lens, B)
+    _need_cuda(q, k_cache, v_cache, block_table, seq_lens, out, lse, workspace)
     dt = BF16 if out_dtype == torch.bfloat16 else FP32 if out_dtype == torch.float32 else None
     if dt is None:
         raise ValueError("out_dtype must be bf16 or fp32")

@@ -4,12 +4,16 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <map>
 #include <mutex>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "backward.h"
 #include "combine.h"
@@ -39,8 +43,18 @@ int ok() {
 constexpr int kMaxDevices = 64;
 std::mutex g_mu;
 int g_arch_ok[kMaxDevices];          // 0 unknown, 1 gfx950, -1 other
-void* g_ws[kMaxDevices];
-size_t g_ws_bytes[kMaxDevices];
+
+// Library-owned workspaces, one per (device, stream): calls on one stream are
+// ordered by that stream, so they may share a buffer; calls on different
+// streams never do. A buffer that becomes too small is retired, not freed:
+// work already enqueued may still use it, and freeing it safely would need a
+// synchronisation. Retired buffers are freed by miattn_release.
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::map<std::pair<int, void*>, Workspace> g_ws;
+std::vector<std::pair<int, void*>> g_ws_retired;   // (device, pointer)
 
 bool arch_is_gfx950(int dev) {
   hipDeviceProp_t p;
@@ -138,27 +152,24 @@ void launch_decode_study(const miattn::DecodeArgs& a, bool rr, bool pf16, hipStr
   }
 }
 
-// The device's library-owned workspace, grown to at least `need` bytes.
-int library_workspace(int dev, size_t need, void** ws, const char* who) {
+// The library-owned workspace of (dev, stream), grown to at least `need`
+// bytes. Growth at least doubles the size, so the retired buffers of a stream
+// never add up to more than its current one.
+int library_workspace(int dev, hipStream_t stream, size_t need, void** ws, const char* who) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (g_ws_bytes[dev] < need) {
-    if (g_ws[dev] != nullptr) {
-      // an enqueued kernel may still read the old buffer
-      if (hipDeviceSynchronize() != hipSuccess || hipFree(g_ws[dev]) != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(MIATTN_ERR_HIP, "%s: releasing the workspace failed", who);
-      }
-      g_ws[dev] = nullptr;
-      g_ws_bytes[dev] = 0;
-    }
-    if (hipMalloc(&g_ws[dev], need) != hipSuccess) {
+  Workspace& w = g_ws[std::make_pair(dev, (void*)stream)];
+  if (w.bytes < need) {
+    size_t bytes = 2 * w.bytes > need ? 2 * w.bytes : need;
+    void* p = nullptr;
+    if (hipMalloc(&p, bytes) != hipSuccess) {
       (void)hipGetLastError();
-      g_ws[dev] = nullptr;
-      return fail(MIATTN_ERR_HIP, "%s: workspace allocation of %zu bytes failed", who, need);
+      return fail(MIATTN_ERR_HIP, "%s: workspace allocation of %zu bytes failed", who, bytes);
     }
-    g_ws_bytes[dev] = need;
+    if (w.ptr != nullptr) g_ws_retired.emplace_back(dev, w.ptr);
+    w.ptr = p;
+    w.bytes = bytes;
   }
-  *ws = g_ws[dev];
+  *ws = w.ptr;
   return MIATTN_OK;
 }
 
@@ -190,6 +201,15 @@ int decode_heads_per_wg(int hkv) {
   return 1;
 }
 
+// The split-count rule of "Why your local LLM feels dumber than it is"
+// (section "Why FlashAttention 2 selects 54, 62, or 87 groups"). Blocks of
+// block_tokens are dealt out in equal runs of ceil(blocks / s), so only the
+// distinct run lengths matter; each is represented by the smallest count that
+// gives it. Walking the run lengths from the longest down, the count after s
+// (run length r) is the first one with a shorter run, ceil(blocks / (r - 1)).
+// A count is scored by the filled fraction of its last wave, f = x / ceil(x)
+// with x = work_units * s / capacity; the smallest count scoring at least
+// threshold times the best score is returned.
 int split_rule(long total_tokens, long work_units, long cu_count, long wg_per_cu, long block_tokens,
                long max_splits, double threshold) {
   if (total_tokens <= 0 || work_units <= 0 || cu_count <= 0 || wg_per_cu <= 0 || block_tokens <= 0 ||
@@ -197,23 +217,23 @@ int split_rule(long total_tokens, long work_units, long cu_count, long wg_per_cu
     return MIATTN_ERR_INVALID_ARG;
   const long blocks = (total_tokens + block_tokens - 1) / block_tokens;
   const long capacity = cu_count * wg_per_cu;
-  long top = max_splits;
-  if (capacity < top) top = capacity;
-  if (blocks < top) top = blocks;
-  double best = 0.0;
-  // pass 1: best efficiency over eligible candidates; pass 2: first within 85%
-  for (int pass = 0; pass < 2; ++pass) {
-    for (long s = 1; s <= top; ++s) {
-      if (s > 1 && (blocks + s - 1) / s == (blocks + s - 2) / (s - 1)) continue;
-      const double ratio = (double)(work_units * s) / (double)capacity;
-      const double eff = ratio / std::ceil(ratio);
-      if (pass == 0) {
-        if (eff > best) best = eff;
-      } else if (eff >= threshold * best) {
-        return (int)s;
-      }
-    }
+  const long limit = std::min(std::min(max_splits, capacity), blocks);
+  auto fill = [&](long s) {
+    const long units = work_units * s;
+    const long waves = (units + capacity - 1) / capacity;
+    return (double)units / (double)(waves * capacity);
+  };
+  std::vector<std::pair<long, double>> cand;   // (count, score), counts rising
+  for (long s = 1; s <= limit;) {
+    cand.emplace_back(s, fill(s));
+    const long run = (blocks + s - 1) / s;
+    if (run <= 1) break;
+    s = (blocks + run - 2) / (run - 1);
   }
+  double best = 0.0;
+  for (const auto& c : cand) best = std::max(best, c.second);
+  for (const auto& c : cand)
+    if (c.second >= threshold * best) return (int)c.first;
   return 1;
 }
 
@@ -257,14 +277,15 @@ void miattn_release(void) {
     (void)hipGetLastError();
     return;
   }
-  for (int d = 0; d < kMaxDevices; ++d) {
-    if (g_ws[d] != nullptr) {
-      (void)hipSetDevice(d);
-      (void)hipFree(g_ws[d]);
-      g_ws[d] = nullptr;
-      g_ws_bytes[d] = 0;
-    }
+  for (auto& kv : g_ws) {
+    if (kv.second.ptr != nullptr) g_ws_retired.emplace_back(kv.first.first, kv.second.ptr);
   }
+  g_ws.clear();
+  for (auto& r : g_ws_retired) {
+    (void)hipSetDevice(r.first);
+    (void)hipFree(r.second);
+  }
+  g_ws_retired.clear();
   (void)hipSetDevice(cur);
 }
 
@@ -423,18 +444,25 @@ int miattn_attn_combine(const float* partial_o, const float* partial_lse, int ro
   return r ? r : ok();
 }
 
-int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
-                             const int32_t* block_table, const int32_t* seq_lens, int batch,
-                             int max_pages_per_seq, int page_size, int num_pages, int num_q_heads,
-                             int num_kv_heads, int head_dim, float scale, int num_splits, void* workspace,
-                             size_t workspace_bytes, void* o, float* lse, void* stream) {
-  if (batch < 0) return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: batch < 0");
-  if (num_splits < 0) return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: num_splits < 0");
+}  // extern "C"
+
+namespace {
+
+// Where the decode's split partials live.
+enum class WsMode { kCaller };
+
+int decode_paged_impl(const char* who, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_table, const int32_t* seq_lens, int batch, int max_pages_per_seq,
+                      int page_size, int num_pages, int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                      int num_splits, WsMode mode, void* workspace, size_t workspace_bytes, void* o, float* lse,
+                      void* stream) {
+  if (batch < 0) return fail(MIATTN_ERR_INVALID_ARG, "%s: batch < 0", who);
+  if (num_splits < 0) return fail(MIATTN_ERR_INVALID_ARG, "%s: num_splits < 0", who);
   if (page_size != MIATTN_PAGE_SIZE)
-    return fail(MIATTN_ERR_UNSUPPORTED, "attn_decode_paged: page_size must be %d", MIATTN_PAGE_SIZE);
+    return fail(MIATTN_ERR_UNSUPPORTED, "%s: page_size must be %d", who, MIATTN_PAGE_SIZE);
   if (batch == 0) return ok();
   {
-    const int r = decode_common_checks("attn_decode_paged", q, k_cache, v_cache, block_table, seq_lens, o,
+    const int r = decode_common_checks(who, q, k_cache, v_cache, block_table, seq_lens, o,
                                        max_pages_per_seq, page_size, num_pages, num_q_heads, num_kv_heads,
                                        head_dim, scale);
     if (r) return r;
@@ -460,20 +488,19 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
   if (S > max_pages_per_seq) S = max_pages_per_seq;   // more splits than pages would only add empty groups
   if (S < 1) S = 1;
   if ((long)S * num_kv_heads * batch > 0x7fffffffL || (long)(units + batch) * num_kv_heads > 0x7fffffffL)
-    return fail(MIATTN_ERR_INVALID_ARG, "attn_decode_paged: splits * Hkv * batch too large");
+    return fail(MIATTN_ERR_INVALID_ARG, "%s: splits * Hkv * batch too large", who);
   // balanced groups: partials of units + batch groups, then the plan table
   const size_t need = units > 0 ? ((((size_t)units + batch) * num_q_heads * ((size_t)head_dim + 1) * sizeof(float) +
                                     2 * (size_t)batch * sizeof(int32_t) + 255) & ~(size_t)255)
                                 : miattn_decode_workspace_bytes(batch, num_q_heads, head_dim, S);
-  if (workspace != nullptr && workspace_bytes < need)
-    return fail(MIATTN_ERR_WORKSPACE, "attn_decode_paged: workspace of %zu bytes, need %zu", workspace_bytes,
-                need);
+  if (mode == WsMode::kCaller && workspace != nullptr && workspace_bytes < need)
+    return fail(MIATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", who, workspace_bytes, need);
   const int dev = current_device();
   if (dev < 0) return dev;
   hipStream_t st = (hipStream_t)stream;
   void* ws = workspace;
   if (need > 0 && ws == nullptr) {
-    const int r = library_workspace(dev, need, &ws, "attn_decode_paged");
+    const int r = library_workspace(dev, st, need, &ws, who);
     if (r) return r;
   }
   miattn::DecodeArgs a{};
@@ -512,6 +539,20 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
     if (r) return r;
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_cache,
+                             const int32_t* block_table, const int32_t* seq_lens, int batch,
+                             int max_pages_per_seq, int page_size, int num_pages, int num_q_heads,
+                             int num_kv_heads, int head_dim, float scale, int num_splits, void* workspace,
+                             size_t workspace_bytes, void* o, float* lse, void* stream) {
+  return decode_paged_impl("attn_decode_paged", q, k_cache, v_cache, block_table, seq_lens, batch,
+                           max_pages_per_seq, page_size, num_pages, num_q_heads, num_kv_heads, head_dim, scale,
+                           num_splits, WsMode::kCaller, workspace, workspace_bytes, o, lse, stream);
 }
 
 namespace {
@@ -556,7 +597,7 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
   hipStream_t st = (hipStream_t)stream;
   void* ws = workspace;
   if (ws == nullptr) {
-    const int r = library_workspace(dev, need, &ws, who);
+    const int r = library_workspace(dev, st, need, &ws, who);
     if (r) return r;
   }
   const long t_pad = bwd_t_pad(total_tokens);
@@ -657,7 +698,7 @@ int miattn_attn_decode_paged_numerics(const void* q, const void* k_cache, const 
   hipStream_t st = (hipStream_t)stream;
   void* ws = workspace;
   if (ws == nullptr) {
-    const int r = library_workspace(dev, need, &ws, who);
+    const int r = library_workspace(dev, st, need, &ws, who);
     if (r) return r;
   }
   const size_t rows = (size_t)batch * num_q_heads;

@@ -28,6 +28,17 @@
  *     bitwise identical from run to run: no floating-point atomics are used and
  *     every reduction has a fixed order.
  *   - Inputs are not checked for NaN/Inf; non-finite inputs propagate.
+ *
+ * Library-owned workspaces (workspace == NULL in the calls that take one)
+ *   The library keeps one scratch buffer per (device, stream) pair: calls on
+ *   the same stream run in stream order and share it; calls on different
+ *   streams use different buffers, so they may overlap. A buffer that is too
+ *   small for a call is replaced by a larger one (at least twice the size);
+ *   the old one is kept, not freed, because work already enqueued may still
+ *   read it, so growth needs no synchronisation. All of them are freed by
+ *   miattn_release. The buffer of a stream handle is reused by a later stream
+ *   that gets the same handle value: destroy a stream only once the library
+ *   calls enqueued on it have finished.
  */
 #ifndef MIATTN_H
 #define MIATTN_H
@@ -157,9 +168,9 @@ int miattn_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cach
  *            fixed inputs.
  *   workspace / workspace_bytes: device scratch for the split partials
  *            (miattn_decode_workspace_bytes bytes). workspace == NULL uses a
- *            buffer the library allocates and caches per device (grown on
- *            demand; freed by miattn_release). Not used when the split count
- *            is 1.
+ *            library-owned buffer (see "Library-owned workspaces" above). Not
+ *            used when the split count is 1. A caller workspace must not be
+ *            in use by another call that may run at the same time.
  * Robustness: seq_lens are clamped to [0, max_pages_per_seq * 16]; a block
  * table entry outside [0, num_pages) makes that page contribute nothing. Such
  * inputs never fault, but their results are unspecified.
@@ -230,7 +241,7 @@ size_t miattn_decode_workspace_bytes(int batch, int num_q_heads, int head_dim, i
  * o [batch, Hq, D] of out_dtype (MIATTN_BF16 or MIATTN_FP32, the latter for
  *   the output before its final rounding); lse [batch, Hq] float32 or NULL.
  * workspace: miattn_decode_numerics_workspace_bytes bytes, or NULL for the
- *   library-owned buffer (shared with miattn_attn_decode_paged).
+ *   library-owned buffer of the stream (shared with its other calls).
  * Other arguments, layouts, limits and errors as for
  * miattn_attn_decode_paged; unknown numerics bits or a bad tile_pages give
  * MIATTN_ERR_UNSUPPORTED.
@@ -271,7 +282,7 @@ size_t miattn_decode_numerics_workspace_bytes(int batch, int num_q_heads, int he
  *   otherwise).
  *   workspace: miattn_attn_bwd_workspace_bytes bytes of device scratch (row
  *   terms and fp16 copies of the inputs), or NULL for the library-owned
- *   buffer. Inputs must lie inside fp16's range (|x| <= 65504): the products
+ *   buffer of the stream. Inputs must lie inside fp16's range (|x| <= 65504): the products
  *   run on fp16 operands, to which bf16 values inside that range convert
  *   exactly.
  * Deterministic: fixed reduction orders, no atomics; dQ is computed by its own
@@ -312,8 +323,9 @@ const char* miattn_last_error(void);
 int miattn_version(void);
 /* 1 if HIP device `device` is a gfx950 the kernels were built for, else 0. */
 int miattn_device_supported(int device);
-/* Free the library-owned workspace cache on every device (safe to call at any
- * time when no call is in flight). */
+/* Free every library-owned workspace on every device, retired ones included.
+ * Call it only when no library work is enqueued or running: it frees memory
+ * that such work may use (hipFree itself waits for the device). */
 void miattn_release(void);
 
 #ifdef __cplusplus

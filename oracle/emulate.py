@@ -113,25 +113,34 @@ def fa2_split_count(total_tokens: int, sm_count: int, kv_heads: int = 4, batch: 
                     block_tokens: int = 64, max_splits: int = 128, blocks_per_sm: int = 2,
                     threshold: float = 0.85):
     """The split-count rule described in "Why FlashAttention 2 selects 54, 62,
-    or 87 groups": capacity = 2 work blocks per streaming multiprocessor; a
-    candidate count s gives work ratio batch*kv_heads*s / capacity and
-    efficiency ratio / ceil(ratio); counts that do not change the number of
-    64-token blocks per split are skipped; the smallest count reaching 85% of
-    the best efficiency wins (`threshold` generalizes the 85%). Returns
-    (splits, key_value_blocks, blocks_per_split)."""
+    or 87 groups". The key/value blocks (64 tokens) are dealt out in equal
+    runs, so a split count only matters through the run length it gives; for
+    every run length that some count up to min(max_splits, capacity, blocks)
+    can give, the count in play is the smallest one giving it. Each such count
+    s is scored by its estimated efficiency, the filled fraction of the last
+    wave when batch*kv_heads*s work units meet a capacity of 2 work blocks per
+    streaming multiprocessor; the smallest count scoring at least 85% of the
+    best score is chosen (`threshold` generalizes the 85%). Scores are exact
+    fractions. Returns (splits, key_value_blocks, blocks_per_split)."""
+    from fractions import Fraction
     n_blocks = -(-total_tokens // block_tokens)
     capacity = blocks_per_sm * sm_count
-    work = batch * kv_heads
-    top = min(max_splits, capacity, n_blocks)
-    cands = []
-    for s in range(1, top + 1):
-        if s > 1 and -(-n_blocks // s) == -(-n_blocks // (s - 1)):
-            continue
-        ratio = work * s / capacity
-        cands.append((s, ratio / math.ceil(ratio)))
-    best = max(e for _, e in cands)
-    s = next(c for c, e in cands if e >= threshold * best)
-    return s, n_blocks, -(-n_blocks // s)
+    units = batch * kv_heads
+    limit = min(max_splits, capacity, n_blocks)
+    # run length -> smallest split count that produces it
+    first_count = {}
+    for s in range(limit, 0, -1):
+        first_count[-(-n_blocks // s)] = s
+    counts = sorted(first_count.values())
+
+    def efficiency(s):
+        waves = Fraction(units * s, capacity)
+        return waves / math.ceil(waves)
+
+    scores = {s: efficiency(s) for s in counts}
+    best = max(scores.values())
+    chosen = min(s for s in counts if scores[s] >= Fraction(threshold).limit_denominator(10 ** 6) * best)
+    return chosen, n_blocks, -(-n_blocks // chosen)
 
 
 def fa2_groups(total_tokens: int, splits: int, block_tokens: int = 64):
@@ -236,23 +245,29 @@ def merge_normalizer_weighted(A: Arithmetic, parts) -> float:
 
 
 def merge_ordered(A: Arithmetic, parts, bf16_numerator: bool = True) -> float:
-    """Running (max, normalizer, numerator) folded over the groups in order;
-    a running state that is still empty (max -inf) contributes nothing, and an
-    empty group (max -inf) is skipped."""
-    run_m = -math.inf
-    run_l = A.dtype(0)
-    run_n = A.dtype(0)
-    for p in parts:
+    """The ordered running recurrence of the TensorRT-LLM reducer ("Backend
+    names expand into four decode algorithms"): a state (max, normalizer,
+    numerator) absorbs the group records one at a time in group order. To
+    absorb a record, both sides are brought to the larger of the two maxima
+    and added; a state that is still empty (max -inf) contributes nothing, and
+    an empty record (max -inf) leaves the state as it is. The numerator of a
+    record enters rounded to bf16 when `bf16_numerator`."""
+    from functools import reduce
+
+    def absorb(state, p):
+        m_run, l_run, n_run = state
         if p.m == -math.inf:
-            continue
-        new_m = max(run_m, p.m)
-        keep = A.dtype(0) if run_m == -math.inf else A.exp(A.r(run_m - new_m))
-        take = A.exp(A.r(p.m - new_m))
-        n_p = A.half(p.num) if bf16_numerator else A.r(p.num)
-        run_l = A.r(A.r(run_l * keep) + A.r(A.r(p.l) * take))
-        run_n = A.r(A.r(run_n * keep) + A.r(n_p * take))
-        run_m = new_m
-    return float(A.r(run_n / run_l))
+            return state
+        top = max(m_run, p.m)
+        w_run = A.dtype(0) if m_run == -math.inf else A.exp(A.r(m_run - top))
+        w_new = A.exp(A.r(p.m - top))
+        num = A.half(p.num) if bf16_numerator else A.r(p.num)
+        return (top,
+                A.r(A.r(l_run * w_run) + A.r(A.r(p.l) * w_new)),
+                A.r(A.r(n_run * w_run) + A.r(num * w_new)))
+
+    _, l_fin, n_fin = reduce(absorb, parts, (-math.inf, A.dtype(0), A.dtype(0)))
+    return float(A.r(n_fin / l_fin))
 
 
 # ----------------------------------------------------------- the four programs

@@ -1,6 +1,11 @@
 """Helpers for the GPU parity tests (test side only)."""
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import torch
+
+import oracle
 
 DEV = torch.device("cuda:0") if torch.cuda.is_available() else None
 
@@ -78,3 +83,30 @@ def assert_lse_close(got, want, what="", tol=LSE_MAX_ABS):
 def bitwise_equal(a, b):
     return torch.equal(a.view(torch.int16) if a.dtype == torch.bfloat16 else a.view(torch.int32),
                        b.view(torch.int16) if b.dtype == torch.bfloat16 else b.view(torch.int32))
+
+
+def dense_oracle_parallel(q, k, v, cu_seqlens, num_q_heads, num_kv_heads, scale, causal, workers=None):
+    """oracle.attention_dense on the whole problem, computed as independent
+    sub-problems (one sequence, one kv head and its query heads) on a thread
+    pool; each sub-problem is the oracle's own call, so the result is the
+    oracle's, only sooner on a many-core host."""
+    T, Hq, _ = q.shape
+    G = num_q_heads // num_kv_heads
+    O = np.zeros((T, Hq, v.shape[2]), dtype=np.float64)
+    L = np.full((Hq, T), -np.inf, dtype=np.float64)
+    cu = [int(x) for x in cu_seqlens]
+    jobs = [(b, g) for b in range(len(cu) - 1) for g in range(num_kv_heads)]
+    jobs.sort(key=lambda j: -(cu[j[0] + 1] - cu[j[0]]))   # longest first
+
+    def one(job):
+        b, g = job
+        s0, s1 = cu[b], cu[b + 1]
+        o, l = oracle.attention_dense(q[s0:s1, g * G:(g + 1) * G], k[s0:s1, g:g + 1], v[s0:s1, g:g + 1],
+                                      np.array([0, s1 - s0]), G, 1, scale, causal)
+        O[s0:s1, g * G:(g + 1) * G] = o
+        L[g * G:(g + 1) * G, s0:s1] = l
+
+    n = workers or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(n) as ex:
+        list(ex.map(one, jobs))
+    return O, L

@@ -318,3 +318,19 @@ def test_bwd_empty_is_noop_and_workspace_size():
     # stats: 2 x 3 heads x 192 padded rows x 4 B = 4608; copies 2 x 100 x 4 x 64 x 2 = 102400
     assert mi.attn_bwd_workspace_bytes(100, 3, 1, 64) == 4608 + 102400
     assert mi.attn_bwd_workspace_bytes(0, 3, 1, 64) == 0
+
+
+@pytest.mark.parametrize("fn", ["attn_decode_paged", "attn_decode_paged_numerics"])
+@pytest.mark.parametrize("bt_shape,sl_shape", [((1, 4), (2,)), ((2, 4), (1,)), ((8,), (2,)), ((2, 4), (2, 1)),
+                                               ((3, 4), (3,))])
+def test_decode_binding_rejects_short_tables(fn, bt_shape, sl_shape):
+    # the kernels read block_table[b, :] and seq_lens[b] for every b < batch:
+    # tables that do not match the batch must be refused before any launch
+    import torch
+    q = torch.zeros((2, 4, 128), dtype=torch.bfloat16)
+    kc = torch.zeros((8, 16, 2, 128), dtype=torch.bfloat16)
+    bt = torch.zeros(bt_shape, dtype=torch.int32)
+    sl = torch.zeros(sl_shape, dtype=torch.int32)
+    kw = dict(scale=0.1, num_splits=2)
+    with pytest.raises(ValueError, match="block_table|seq_lens"):
+        getattr(mi, fn)(q, kc, kc, bt, sl, **kw)

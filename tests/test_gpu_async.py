@@ -1,0 +1,82 @@
+"""The library enqueues and returns: a call that has to grow its library-owned
+workspace does not wait for work running on another stream, and calls on
+different streams use different library-owned workspaces."""
+import math
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import attention_attn_fwd_03_amd as mi
+import oracle
+import synth
+from gpu_util import assert_bf16_close, bf16_dev, bitwise_equal, host, i32_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def dec_dev(case):
+    return (bf16_dev(case.q), bf16_dev(case.k_cache), bf16_dev(case.v_cache), i32_dev(case.block_table),
+            i32_dev(case.seq_lens))
+
+
+def test_workspace_growth_does_not_wait_for_other_streams():
+    # a long prefill (varlen head_dim 256, ~2.7 ms a launch, 4 launches) on
+    # stream A; then, on a fresh stream B, a decode whose library-owned
+    # workspace does not exist yet and must be allocated
+    pf = synth.config5(seed=0)
+    q, k, v = bf16_dev(pf.q), bf16_dev(pf.k), bf16_dev(pf.v)
+    cu = i32_dev(pf.cu_seqlens)
+    dc = synth.config4(ctx=16384, seed=0)
+    dd = dec_dev(dc)
+    a, b = torch.cuda.Stream(), torch.cuda.Stream()
+    # load both kernels once, outside the measured window
+    with torch.cuda.stream(a):
+        mi.attn_fwd(q, k, v, cu, pf.max_seqlen, scale=pf.scale, causal=True)
+    ws = torch.empty(mi.decode_workspace_bytes(1, 16, 256, 16), dtype=torch.uint8, device="cuda")
+    mi.attn_decode_paged(*dd, scale=dc.scale, num_splits=16, workspace=ws)
+    torch.cuda.synchronize()
+
+    done = torch.cuda.Event()
+    with torch.cuda.stream(a):
+        for _ in range(4):
+            mi.attn_fwd(q, k, v, cu, pf.max_seqlen, scale=pf.scale, causal=True)
+        done.record(a)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(b):
+        o, l = mi.attn_decode_paged(*dd, scale=dc.scale, num_splits=16)   # workspace=None: grows B's buffer
+    t1 = time.perf_counter()
+    still_running = not done.query()
+    print(f"  decode call returned after {1e3 * (t1 - t0):.3f} ms; prefill still running: {still_running}",
+          flush=True)
+    assert still_running, "the decode call waited for the other stream's work"
+    torch.cuda.synchronize()
+    qd, kc, vc = dc.as_f64()
+    O, _ = oracle.decode_dense(qd, kc, vc, dc.block_table, dc.seq_lens, dc.scale)
+    assert_bf16_close(host(o), O, "decode on stream B")
+
+
+def test_streams_do_not_share_library_workspace():
+    # two different problems with the same split count, enqueued alternately
+    # on two streams with no synchronisation between them: each result must
+    # equal the one computed alone
+    c1 = synth.make_decode(3, 11, [4000, 3000, 2500, 1000], 32, 8, 128, 1 / math.sqrt(128), shuffle=True,
+                           tail="zero", name="streams_a")
+    c2 = synth.make_decode(3, 12, [3900, 100, 2600, 4096], 32, 8, 128, 1 / math.sqrt(128), shuffle=True,
+                           tail="zero", name="streams_b")
+    d1, d2 = dec_dev(c1), dec_dev(c2)
+    r1 = mi.attn_decode_paged(*d1, scale=c1.scale, num_splits=8)
+    r2 = mi.attn_decode_paged(*d2, scale=c2.scale, num_splits=8)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for _ in range(8):
+        with torch.cuda.stream(s1):
+            outs.append((1, mi.attn_decode_paged(*d1, scale=c1.scale, num_splits=8)))
+        with torch.cuda.stream(s2):
+            outs.append((2, mi.attn_decode_paged(*d2, scale=c2.scale, num_splits=8)))
+    torch.cuda.synchronize()
+    for which, (o, l) in outs:
+        ref = r1 if which == 1 else r2
+        assert bitwise_equal(o, ref[0]) and bitwise_equal(l, ref[1]), which
