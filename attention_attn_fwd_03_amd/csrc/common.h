@@ -131,4 +131,29 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u32x2 a, u32x2 b) {
 }
 __device__ __forceinline__ bf16x4 as_bf16x4(u32x2 v) { return __builtin_bit_cast(bf16x4, v); }
 
+// Probabilities for the P.V product: two floats -> a packed pair of fp16
+// (F16) or bf16, round to nearest even.
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_p(float lo, float hi) {
+  if constexpr (F16) return pack_f16x2(lo, hi);
+  else return pack_bf16x2(lo, hi);
+}
+// O^T += V^T P^T on 32x32x16 MFMAs: V^T operand halves lo/hi and P operand p
+// in fp16 (F16) or bf16.
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma_pv(u32x2 lo, u32x2 hi, u32x4 p, f32x16 acc) {
+  if constexpr (F16) return __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(lo, hi), as_f16x8(p), acc, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lo, hi), as_bf16x8(p), acc, 0, 0, 0);
+}
+
+// bf16 -> fp16 copy of n8 groups of eight elements (16 bytes each), one
+// group per thread and grid stride: exact for magnitudes in [2^-14, 65504];
+// smaller ones become fp16 subnormals (absolute error at most 2^-25), larger
+// ones overflow to inf.
+__global__ __launch_bounds__(256) void miattn_bf16_to_f16_kernel(const uint16_t* __restrict__ src,
+                                                                 uint16_t* __restrict__ dst, long n8) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256)
+    st16(dst + 8 * i, bf16x8_to_f16x8(ld16_stream(src + 8 * i)));
+}
+
 }  // namespace miattn

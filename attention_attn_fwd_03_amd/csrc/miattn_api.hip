@@ -89,15 +89,16 @@ int check_launch(const char* what) {
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
 // --- prefill launches ------------------------------------------------------
-template <int D, int QB, int KB, bool CAUSAL, bool PAGED>
+template <int D, int QB, int KB, bool CAUSAL, bool PAGED, bool F16V>
 void launch_fwd(const miattn::FwdArgs& a, int grid, hipStream_t st) {
-  hipLaunchKernelGGL((miattn::miattn_prefill_fwd_kernel<D, QB, KB, CAUSAL, PAGED>), dim3(grid), dim3(256), 0, st, a);
+  hipLaunchKernelGGL((miattn::miattn_prefill_fwd_kernel<D, QB, KB, CAUSAL, PAGED, F16V>), dim3(grid), dim3(256), 0,
+                     st, a);
 }
 
-template <int D, int QB, int KB, bool PAGED = false>
+template <int D, int QB, int KB, bool PAGED = false, bool F16V = false>
 void launch_fwd_c(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t st) {
-  if (causal) launch_fwd<D, QB, KB, true, PAGED>(a, grid, st);
-  else launch_fwd<D, QB, KB, false, PAGED>(a, grid, st);
+  if (causal) launch_fwd<D, QB, KB, true, PAGED, F16V>(a, grid, st);
+  else launch_fwd<D, QB, KB, false, PAGED, F16V>(a, grid, st);
 }
 
 // query blocks of 32 rows per wave for each head_dim
@@ -108,13 +109,18 @@ constexpr int fwd_qb(int d) { return d >= 256 ? 1 : 1; }
 // prefill run the four-wave kernel, which measured faster there.
 constexpr bool fwd_pingpong(int d, bool paged) { return d <= 128 && !paged; }
 
-template <int D, int KB>
+template <int D, int KB, bool F16V>
 void launch_fwd_pp(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t st) {
   if (causal)
-    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, KB, true>), dim3(grid), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, KB, true, F16V>), dim3(grid), dim3(512), 0, st, a);
   else
-    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, KB, false>), dim3(grid), dim3(512), 0, st, a);
+    hipLaunchKernelGGL((miattn::miattn_prefill_pp_kernel<D, KB, false, F16V>), dim3(grid), dim3(512), 0, st, a);
 }
+
+// Dense bf16 prefill whose P.V product runs on fp16 operands: V is first
+// converted to fp16 into a workspace by one streaming pass, and the
+// probabilities are rounded to fp16 instead of bf16.
+constexpr bool fwd_f16v(int d) { return d >= 256; }
 
 // bf16 prefill grid: (head slot, query-tile pair, sequence)
 long fwd_setup(miattn::FwdArgs& a, int num_seqs, int max_seqlen, int num_q_heads, int num_kv_heads, int head_dim,
@@ -367,10 +373,28 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
   const long grid = fwd_setup(a, num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim);
   if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: problem too large");
   const bool cz = causal != 0;
+  if (fwd_f16v(head_dim)) {
+    // V -> fp16 into the stream's library-owned workspace, then the kernel
+    // reads that copy
+    const long n8 = (long)total_tokens * num_kv_heads * head_dim / 8;
+    void* ws = nullptr;
+    const int rw = library_workspace(dev, st, (size_t)n8 * 16, &ws, "attn_fwd");
+    if (rw) return rw;
+    const long blocks = std::min((n8 + 255) / 256, 4096L);
+    hipLaunchKernelGGL(miattn::miattn_bf16_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, st,
+                       (const uint16_t*)v, (uint16_t*)ws, n8);
+    a.v = (const uint16_t*)ws;
+  }
   switch (head_dim) {
-    case 64: launch_fwd_pp<64, 2>(a, (int)grid, cz, st); break;
-    case 128: launch_fwd_pp<128, 2>(a, (int)grid, cz, st); break;
-    default: launch_fwd_c<256, fwd_qb(256), 1>(a, (int)grid, cz, st); break;
+    case 64:
+      if (fwd_f16v(64)) launch_fwd_pp<64, 2, true>(a, (int)grid, cz, st);
+      else launch_fwd_pp<64, 2, false>(a, (int)grid, cz, st);
+      break;
+    case 128:
+      if (fwd_f16v(128)) launch_fwd_pp<128, 2, true>(a, (int)grid, cz, st);
+      else launch_fwd_pp<128, 2, false>(a, (int)grid, cz, st);
+      break;
+    default: launch_fwd_c<256, fwd_qb(256), 1, false, fwd_f16v(256)>(a, (int)grid, cz, st); break;
   }
   const int r = check_launch("prefill bf16");
   return r ? r : ok();

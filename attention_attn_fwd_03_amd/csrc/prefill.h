@@ -94,8 +94,9 @@ struct FwdTile {
 // PAGED: keys/values come from a paged cache through the block table, the
 // sequence's Lk keys end with its Lq queries (chunked prefill), and causal
 // masking aligns the queries to the end: query i sees keys j <= i + Lk - Lq.
-template <int D, int QB, int KB, bool CAUSAL, bool PAGED = false>
+template <int D, int QB, int KB, bool CAUSAL, bool PAGED = false, bool F16V = false>
 __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_prefill_fwd_kernel(FwdArgs a) {
+  static_assert(!(PAGED && F16V), "the fp16 form of V is made for contiguous V only");
   using TL = FwdTile<D, KB>;
   constexpr int BC = TL::BC;
   constexpr int CH = TL::CH;
@@ -336,7 +337,7 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
                 const float p0 = exp2_hw(__builtin_fmaf(s[qb][kb][r], c, nmu));
                 const float p1 = exp2_hw(__builtin_fmaf(s[qb][kb][r + 1], c, nmu));
                 ls[qb] += p0 + p1;
-                pw[qb][kb][r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
+                pw[qb][kb][r >> 3][(r >> 1) & 3] = pack_p<F16V>(p0, p1);
               }
           }
         };
@@ -402,11 +403,8 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
               const int ch = col >> 3, sub = (col & 7) * 2;             // chunk, byte offset in it
               const u32x2 lo = lds_ld_tr16(vl + r0 * (2 * D) + 16 * (ch ^ TL::vswz(r0)) + sub);
               const u32x2 hi = lds_ld_tr16(vl + r1 * (2 * D) + 16 * (ch ^ TL::vswz(r1)) + sub);
-              const bf16x8 vop = as_bf16x8(lo, hi);
 #pragma unroll
-              for (int qb = 0; qb < QB; ++qb) {
-                acc[qb][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop, as_bf16x8(pw[qb][kb][u]), acc[qb][dt], 0, 0, 0);
-              }
+              for (int qb = 0; qb < QB; ++qb) acc[qb][dt] = mfma_pv<F16V>(lo, hi, pw[qb][kb][u], acc[qb][dt]);
             }
           }
         }

@@ -54,7 +54,7 @@ __device__ __forceinline__ void pp_mfma_reads() {
   }
 }
 
-template <int D, int KB, bool CAUSAL>
+template <int D, int KB, bool CAUSAL, bool F16V = false>
 __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
   constexpr int BC = 32 * KB;   // keys per tile
   using TL = FwdTile<D, KB>;
@@ -226,8 +226,7 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
               const MIATTN_LDS uint8_t* vp = vl + (((uint32_t)(64 * dt)) ^ v_x) + (32 * kb + 16 * u) * (2 * D);
               const u32x2 lo = lds_ld_tr16(vp);
               const u32x2 hi = lds_ld_tr16(vp + 8 * (2 * D));
-              acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(lo, hi), as_bf16x8(pw[kb][u]), acc[dt],
-                                                                0, 0, 0);
+              acc[dt] = mfma_pv<F16V>(lo, hi, pw[kb][u], acc[dt]);
             }
           }
         pp_mfma_reads<KB * 2 * NDT, 2, 8>();
@@ -277,7 +276,7 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
             const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, nmu));
             const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, nmu));
             ls += p0 + p1;
-            pw[kb][r >> 3][(r >> 1) & 3] = pack_bf16x2(p0, p1);
+            pw[kb][r >> 3][(r >> 1) & 3] = pack_p<F16V>(p0, p1);
           }
         return ls;
       };

@@ -29,7 +29,8 @@
  *     every reduction has a fixed order.
  *   - Inputs are not checked for NaN/Inf; non-finite inputs propagate.
  *
- * Library-owned workspaces (workspace == NULL in the calls that take one)
+ * Library-owned workspaces (workspace == NULL in the calls that take one,
+ * and the fp16 copy of V made by miattn_attn_fwd at head_dim 256)
  *   The library keeps one scratch buffer per (device, stream) pair: calls on
  *   the same stream run in stream order and share it; calls on different
  *   streams use different buffers, so they may overlap. A buffer that is too
@@ -85,9 +86,14 @@ extern "C" {
  *        counted from each sequence's start; queries and keys coincide).
  *   dtype: MIATTN_BF16 with head_dim 64, 128 or 256, or MIATTN_FP32 with
  *        head_dim 64. bf16 inputs are multiplied on bf16 MFMA with fp32
- *        accumulation; softmax state is fp32; the probabilities enter the P.V
- *        product rounded to bf16 and O is rounded to bf16 once at the end.
- *        fp32 inputs stay fp32 throughout (fp32 MFMA).
+ *        accumulation; softmax state is fp32; O is rounded to bf16 once at
+ *        the end; the row sums add the unrounded fp32 probabilities. In the
+ *        P.V product the probabilities enter rounded to bf16 at head_dim 64
+ *        and 128; at head_dim 256 they enter rounded to fp16 and V is first
+ *        converted to fp16 by one streaming pass into the library-owned
+ *        workspace of the stream (exact for |v| <= 65504, the domain of V at
+ *        head_dim 256; values below 2^-14 become fp16 subnormals, error at
+ *        most 2^-25). fp32 inputs stay fp32 throughout (fp32 MFMA).
  *   LSE_i = max_j s_ij + ln sum_j exp(s_ij - max_j s_ij).
  * num_seqs == 0 or total_tokens == 0 is a no-op returning MIATTN_OK.
  */
