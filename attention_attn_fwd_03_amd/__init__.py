@@ -11,6 +11,8 @@ Entry points (same names as the C ABI, without the ``miattn_`` prefix):
                    max_seqlen_q, *, scale, causal) -> (o, lse)
     attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale,
                       num_splits=0) -> (o, lse)
+    attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, *,
+                              scale, num_splits=0) -> (o, lse)
     attn_decode_paged_numerics(..., *, scale, num_splits, numerics,
                                tile_pages, out_dtype) -> (o, lse)
     attn_combine(partial_o, partial_lse, *, out_dtype) -> (o, lse)
@@ -52,6 +54,8 @@ def _load():
     lib.miattn_attn_fwd_paged.restype = I
     lib.miattn_attn_decode_paged.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, Z, P, P, P]
     lib.miattn_attn_decode_paged.restype = I
+    lib.miattn_attn_decode_paged_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, P, P, P]
+    lib.miattn_attn_decode_paged_noalloc.restype = I
     lib.miattn_attn_decode_paged_numerics.argtypes = [P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, I, P, Z, P,
                                                       I, P, P]
     lib.miattn_attn_decode_paged_numerics.restype = I
@@ -240,6 +244,36 @@ def attn_decode_paged(q, k_cache, v_cache, block_table, seq_lens, *, scale: floa
                                         _ptr(seq_lens), B, block_table.shape[1], page, num_pages, Hq, Hkv,
                                         D, float(scale), int(num_splits), _ptr(workspace), ws_bytes,
                                         _ptr(o), _ptr(lse) if return_lse else None, _stream(q.device)))
+    return o, (lse if return_lse else None)
+
+
+# bytes of the static device scratch behind attn_decode_paged_noalloc
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def attn_decode_paged_noalloc(q, k_cache, v_cache, block_table, seq_lens, *, scale: float, num_splits: int = 0,
+                              out=None, lse=None, return_lse: bool = True):
+    """attn_decode_paged without any device allocation inside the library: the
+    split partials use the library's static per-GPU scratch
+    (NOALLOC_SCRATCH_BYTES). Pass `out` (and `lse`) to allocate nothing here
+    either. Calls that may overlap on one GPU race on that scratch."""
+    B, Hq, D = q.shape
+    num_pages, page, Hkv, Dk = k_cache.shape
+    if q.dtype != torch.bfloat16 or k_cache.dtype != torch.bfloat16 or v_cache.dtype != torch.bfloat16:
+        raise ValueError("decode takes bf16 q and caches")
+    if v_cache.shape != k_cache.shape or Dk != D:
+        raise ValueError("cache shapes do not match q")
+    if block_table.dtype != torch.int32 or seq_lens.dtype != torch.int32:
+        raise ValueError("block_table and seq_lens must be int32")
+    _check_decode_tables(block_table, seq_lens, B)
+    _need_cuda(q, k_cache, v_cache, block_table, seq_lens, out, lse)
+    o = out if out is not None else torch.empty_like(q)
+    if return_lse and lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check(lib.miattn_attn_decode_paged_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_table),
+                                                _ptr(seq_lens), B, block_table.shape[1], page, num_pages, Hq,
+                                                Hkv, D, float(scale), int(num_splits), _ptr(o),
+                                                _ptr(lse) if return_lse else None, _stream(q.device)))
     return o, (lse if return_lse else None)
 
 

@@ -21,6 +21,13 @@
 #include "prefill.h"
 #include "prefill_pp.h"
 
+// Device scratch of the no-allocation decode entry point: one copy per GPU,
+// held until the process ends. In host code `scratch` is only a stand-in for
+// the symbol, not a device address: its address on a device comes from
+// hipGetSymbolAddress (static_scratch below), once per device, and only that
+// address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[MIATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_last_error;
@@ -176,6 +183,25 @@ int library_workspace(int dev, hipStream_t stream, size_t need, void** ws, const
     w.bytes = bytes;
   }
   *ws = w.ptr;
+  return MIATTN_OK;
+}
+
+// Device address of `scratch` on each device (null until looked up).
+void* g_scratch_ptr[kMaxDevices];
+
+int static_scratch(int dev, void** ptr, const char* who) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return fail(MIATTN_ERR_HIP, "%s: hipGetSymbolAddress of the static scratch failed: %s", who,
+                  hipGetErrorString(e));
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
   return MIATTN_OK;
 }
 
@@ -473,7 +499,7 @@ int miattn_attn_combine(const float* partial_o, const float* partial_lse, int ro
 namespace {
 
 // Where the decode's split partials live.
-enum class WsMode { kCaller };
+enum class WsMode { kCaller, kStaticScratch };
 
 int decode_paged_impl(const char* who, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_table, const int32_t* seq_lens, int batch, int max_pages_per_seq,
@@ -519,11 +545,20 @@ int decode_paged_impl(const char* who, const void* q, const void* k_cache, const
                                 : miattn_decode_workspace_bytes(batch, num_q_heads, head_dim, S);
   if (mode == WsMode::kCaller && workspace != nullptr && workspace_bytes < need)
     return fail(MIATTN_ERR_WORKSPACE, "%s: workspace of %zu bytes, need %zu", who, workspace_bytes, need);
+  if (mode == WsMode::kStaticScratch && need > (size_t)MIATTN_NOALLOC_SCRATCH_BYTES)
+    return fail(MIATTN_ERR_WORKSPACE, "%s: the split partials need %zu bytes, the static scratch holds %zu", who,
+                need, (size_t)MIATTN_NOALLOC_SCRATCH_BYTES);
   const int dev = current_device();
   if (dev < 0) return dev;
   hipStream_t st = (hipStream_t)stream;
   void* ws = workspace;
-  if (need > 0 && ws == nullptr) {
+  if (mode == WsMode::kStaticScratch) {
+    ws = nullptr;
+    if (need > 0) {
+      const int r = static_scratch(dev, &ws, who);
+      if (r) return r;
+    }
+  } else if (need > 0 && ws == nullptr) {
     const int r = library_workspace(dev, st, need, &ws, who);
     if (r) return r;
   }
@@ -577,6 +612,16 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
   return decode_paged_impl("attn_decode_paged", q, k_cache, v_cache, block_table, seq_lens, batch,
                            max_pages_per_seq, page_size, num_pages, num_q_heads, num_kv_heads, head_dim, scale,
                            num_splits, WsMode::kCaller, workspace, workspace_bytes, o, lse, stream);
+}
+
+int miattn_attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens, int batch,
+                                     int max_pages_per_seq, int page_size, int num_pages, int num_q_heads,
+                                     int num_kv_heads, int head_dim, float scale, int num_splits, void* o,
+                                     float* lse, void* stream) {
+  return decode_paged_impl("attn_decode_paged_noalloc", q, k_cache, v_cache, block_table, seq_lens, batch,
+                           max_pages_per_seq, page_size, num_pages, num_q_heads, num_kv_heads, head_dim, scale,
+                           num_splits, WsMode::kStaticScratch, nullptr, 0, o, lse, stream);
 }
 
 namespace {

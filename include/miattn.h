@@ -189,6 +189,31 @@ int miattn_attn_decode_paged(const void* q, const void* k_cache, const void* v_c
                              void* o, float* lse, void* stream);
 
 /*
+ * miattn_attn_decode_paged_noalloc -- miattn_attn_decode_paged for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. It calls no hipMalloc, hipFree or
+ * allocating library routine. The split partials go to a static device
+ * buffer of MIATTN_NOALLOC_SCRATCH_BYTES that the library holds on every GPU
+ * it runs on until the process ends; its address is looked up once per
+ * device, on the first call made there.
+ *   Arguments, layouts, split plan, numerics and results are those of
+ *   miattn_attn_decode_paged (bitwise the same outputs) without the
+ *   workspace pair. A call whose partials would need more than
+ *   MIATTN_NOALLOC_SCRATCH_BYTES (miattn_decode_workspace_bytes for the
+ *   resolved split count) returns MIATTN_ERR_WORKSPACE and enqueues nothing.
+ *   Every call on one GPU uses the same buffer, whatever its stream: calls
+ *   that may run at the same time on one GPU (other streams, other threads)
+ *   race and give wrong results. Nothing in the buffer needs to start at
+ *   zero: each call writes every partial it reads.
+ */
+#define MIATTN_NOALLOC_SCRATCH_BYTES (32u << 20)
+int miattn_attn_decode_paged_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                     const int32_t* block_table, const int32_t* seq_lens,
+                                     int batch, int max_pages_per_seq, int page_size, int num_pages,
+                                     int num_q_heads, int num_kv_heads, int head_dim, float scale,
+                                     int num_splits, void* o, float* lse, void* stream);
+
+/*
  * miattn_attn_combine -- merge split partials by log-sum-exp weights (the
  * FlashAttention 2 merge of "Why your local LLM feels dumber than it is",
  * section "Backend names expand into four decode algorithms"):
