@@ -10,6 +10,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "miattn_api.hip")
 LIB = os.path.join(HERE, "libmiattn.so")
+# matrix-core rate probe used by bench.py --mfma-peak (not part of the library)
+PEAK_SRC = os.path.join(HERE, "csrc", "mfma_peak.hip")
+PEAK_LIB = os.path.join(HERE, "libmiattn_peak.so")
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -29,10 +32,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile the library; always recompiles. Returns the path of the .so."""
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, SRC]
+def _compile(src: str, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
+    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-o", tmp, src]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
@@ -40,7 +42,14 @@ def build(verbose: bool = False) -> str:
                     if "packed-fp32-ops" not in line and "unknown target feature" not in line)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{out}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the library and the matrix-core probe; always recompiles.
+    Returns the path of the library."""
+    _compile(SRC, LIB, verbose)
+    _compile(PEAK_SRC, PEAK_LIB, verbose)
     return LIB
 
 

@@ -243,17 +243,28 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
 
   // K/V rows of the wave's i-th page into registers; returns the physical
   // page (-1: contributes nothing). The page must lie in the current
-  // block-table window. Loads never branch: an invalid page reads page 0 and
-  // its values are masked (K) or zeroed (V) before use.
-  auto load_page = [&](int i, u32x4* kb, u32x4* vb) -> int {
+  // block-table window. The loads are buffer loads with the page as the
+  // buffer (its base uniform, lane offsets inside it), so they never branch:
+  // for an invalid page, or a prefetch past the wave's last page (`real`
+  // false, uniform), the buffer is empty and every load returns zeros without
+  // touching memory; those values are masked (K) or zeroed (V) before use,
+  // or never used.
+  const uint32_t page_bytes = (uint32_t)(page_stride * 2);
+  const uint32_t lane_off = (uint32_t)(((size_t)lrow * row_stride + (size_t)g * D + 8 * lch) * 2);
+  auto load_page = [&](int i, bool real, u32x4* kb, u32x4* vb) -> int {
     const int pp = phys_page(i);
-    const uint16_t* kp = a.k_cache + (size_t)(pp >= 0 ? pp : 0) * page_stride + (size_t)lrow * row_stride
-                         + (size_t)g * D + 8 * lch;
-    const uint16_t* vp = a.v_cache + (kp - a.k_cache);
+    const size_t base = (size_t)(pp >= 0 ? pp : 0) * page_stride;
+    const int nrec = (real && pp >= 0) ? (int)page_bytes : 0;
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.k_cache + base), (short)0, nrec, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(a.v_cache + base), (short)0, nrec, 0x00020000);
 #pragma unroll
     for (int j = 0; j < NKK; ++j) {
-      kb[j] = ld16_stream(kp + (size_t)(RPI * j) * row_stride);
-      vb[j] = ld16_stream(vp + (size_t)(RPI * j) * row_stride);
+      const int o = (int)(lane_off + (uint32_t)(RPI * j * row_stride * 2));
+      // cache policy 2: non-temporal, the data is read once
+      kb[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kr, o, 0, 2));
+      vb[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vr, o, 0, 2));
     }
     return pp;
   };
@@ -332,17 +343,17 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
   };
 
   // Pages are walked in windows of 64 (one block-table entry per lane).
-  // Inside a window every load is unconditional: the prefetch past the last
-  // page re-reads that page and a uniform branch skips its accumulation, so
-  // the compiler can count outstanding loads exactly and wait only for the
-  // page about to be used.
+  // Inside a window every load is issued unconditionally: the prefetch past
+  // the last page is an empty-buffer load (no memory traffic) and a uniform
+  // branch skips its accumulation, so the compiler can count outstanding
+  // loads exactly and wait only for the page about to be used.
   for (int w0 = 0; w0 < np; w0 += 64) {
     const int n_in = np - w0 < 64 ? np - w0 : 64;
     load_bt_window(w0);
     u32x4 kb[PF][NKK], vb[PF][NKK];
     int pp_buf[PF];
 #pragma unroll
-    for (int j = 0; j < PF; ++j) pp_buf[j] = load_page(w0 + (j < n_in ? j : n_in - 1), kb[j], vb[j]);
+    for (int j = 0; j < PF; ++j) pp_buf[j] = load_page(w0 + (j < n_in ? j : n_in - 1), j < n_in, kb[j], vb[j]);
     for (int i0 = 0; i0 < n_in; i0 += PF) {
 #pragma unroll
       for (int j = 0; j < PF; ++j) {
@@ -350,8 +361,8 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
         const bool live = ii < n_in;            // uniform
         const bool ok_i = live && pp_buf[j] >= 0;
         stage(w0 + ii, ok_i, kb[j], vb[j]);
-        const int nxt = ii + PF < n_in ? ii + PF : n_in - 1;
-        pp_buf[j] = load_page(w0 + nxt, kb[j], vb[j]);
+        const bool more = ii + PF < n_in;       // uniform: a page is left to fetch
+        pp_buf[j] = load_page(w0 + (more ? ii + PF : n_in - 1), more, kb[j], vb[j]);
         if (live) accumulate(w0 + ii, scores(), ok_i);
       }
     }

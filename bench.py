@@ -108,20 +108,27 @@ def sweep_splits(torch, mi, dev):
         q = torch.randn((len(lens), Hq, D), generator=g, device=dev).to(torch.bfloat16)
         return q, kc, vc, bt, torch.tensor(lens, dtype=torch.int32, device=dev)
 
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+
     def time_it(args, S, scale):
+        # per-call events; a working set below 512 MB (twice the last-level
+        # cache) is evicted by a 512 MB read before each call, outside the
+        # events, so its K/V come from HBM
+        cold = 4 * args[1].numel() < 512e6
         for _ in range(3):
             mi.attn_decode_paged(*args, scale=scale, num_splits=S)
         torch.cuda.synchronize()
-        ts = []
-        for _ in range(5):
+        evs = []
+        for i in range(40):
+            if cold:
+                flush.max()   # read-only: leaves no dirty lines behind
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            for _ in range(20):
-                mi.attn_decode_paged(*args, scale=scale, num_splits=S)
+            mi.attn_decode_paged(*args, scale=scale, num_splits=S)
             e1.record()
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) / 20 * 1e3)
-        return statistics.median(ts)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return statistics.median([a.elapsed_time(b) * 1e3 for a, b in evs])
 
     for Hq, Hkv, D in ((32, 8, 128), (16, 4, 256)):
         for B in (1, 4, 16, 64):
@@ -199,6 +206,188 @@ def numerics_timing(torch, mi, dev, bf16, i32, steps: int, warmup: int):
                               "time_vs_fast_path": round(us / base, 3)}), flush=True)
         del args
         torch.cuda.empty_cache()
+
+
+def mfma_peak(torch, dev, iters: int = 2000):
+    """Matrix-core rate of this chip: back-to-back 32x32x16 bf16 MFMAs on
+    register operands (libmiattn_peak.so), over 1-16 independent accumulator
+    chains and 1, 2 or 4 workgroups of four waves per compute unit; one JSON
+    line per cell, then the best rate beside the published dense peak."""
+    import ctypes
+    from attention_attn_fwd_03_amd.build import PEAK_LIB
+    lib = ctypes.CDLL(PEAK_LIB)
+    lib.miattn_probe_mfma_peak.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, ctypes.c_void_p]
+    lib.miattn_probe_mfma_peak.restype = ctypes.c_int
+    # bf16 operands near 1.0 (bit patterns 0x3f80 + small offsets): finite sums
+    seed = (torch.arange(32, dtype=torch.int32, device=dev) + 0x3F80).contiguous()
+    st = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    best = None
+    for chains in (1, 2, 4, 8, 16):
+        for blocks in (256, 512, 1024):
+            out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+
+            def run(n):
+                rc = lib.miattn_probe_mfma_peak(ctypes.c_void_p(seed.data_ptr()), ctypes.c_void_p(out.data_ptr()),
+                                                blocks, n, chains, st)
+                assert rc == 0, rc
+            t_end = time.perf_counter() + 0.2   # settle the clock under this load
+            while time.perf_counter() < t_end:
+                run(iters)
+                torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            run(iters)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            tf = blocks * 4 * iters * 16 * 32768 / (ms * 1e-3) / 1e12
+            cell = {"probe": "mfma_f32_32x32x16_bf16, register operands", "chains": chains,
+                    "workgroups": blocks, "waves_per_simd": blocks // 256, "ms": round(ms, 4),
+                    "TFLOP/s": round(tf, 1), "frac_of_2500": round(tf / PEAK_BF16_TFLOPS, 4)}
+            print(json.dumps(cell), flush=True)
+            if best is None or tf > best["TFLOP/s"]:
+                best = cell
+    print(json.dumps({"mfma_peak_best": best, "published_dense_bf16_TFLOP/s": PEAK_BF16_TFLOPS}), flush=True)
+
+
+def cells(torch, mi, dev, bf16, i32, f32, oracle_too: bool):
+    """Every cell of the measurement table, one op per cell: 10 warmups, then
+    each call bracketed by its own HIP events (median and min reported). Cells
+    whose working set is below 512 MB (twice the 256 MB last-level cache) get a
+    512 MB read of a scratch buffer before each timed call, outside the
+    events, so their inputs come from HBM (a read, not a write: written lines
+    would still be draining to HBM during the timed call). With `oracle_too`, the fp64 oracle
+    is timed on the host on a bounded sample of each workload."""
+    import statistics
+    import oracle
+    import synth
+    from attention_attn_fwd_03_amd import accounting
+    flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+
+    def timed(f, n, cold):
+        for _ in range(10):
+            f()
+        torch.cuda.synchronize()
+        evs = []
+        for i in range(n):
+            if cold:
+                flush.max()   # read-only: leaves no dirty lines behind
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            f()
+            e1.record()
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        us = [a.elapsed_time(b) * 1e3 for a, b in evs]
+        return statistics.median(us), min(us)
+
+    def oracle_time(fn, work, unit, sample, min_s=2.0):
+        reps, tot = 0, 0.0
+        while reps == 0 or (tot < min_s and reps < 5):
+            t0 = time.perf_counter()
+            fn()
+            tot += time.perf_counter() - t0
+            reps += 1
+        return {"value": work * reps / tot / (1e12 if unit == "TFLOP/s" else 1e9), "unit": unit,
+                "sample": sample, "reps": reps, "s": round(tot, 2)}
+
+    def emit(d):
+        print(json.dumps(d), flush=True)
+
+    # config 1: dense fp32, one head, 256 tokens, non-causal (latency)
+    c1 = synth.config1(0)
+    a1 = (f32(c1.q), f32(c1.k), f32(c1.v), i32(c1.cu_seqlens))
+
+    def f1():
+        mi.attn_fwd(*a1, c1.max_seqlen, scale=c1.scale, causal=False)
+    warm, _ = timed(f1, 200, False)
+    cold, mn = timed(f1, 200, True)
+    d = {"cell": "config1 fp32 dense S=256 D=64", "us_median_warm": round(warm, 2), "us_median_cold": round(cold, 2),
+         "us_min_cold": round(mn, 2), "bound": "latency"}
+    if oracle_too:
+        q, k, v = c1.as_f64()
+        d["oracle"] = oracle_time(lambda: oracle.attention_dense(q, k, v, c1.cu_seqlens, 1, 1, c1.scale, False),
+                                  accounting.prefill_flops(c1.seqlens, 1, 64, False), "TFLOP/s", "whole workload")
+    emit(d)
+
+    # config 2: causal GQA prefill at S = 1024, 2048, 4096
+    for S in (1024, 2048, 4096):
+        c = synth.config2(S=S, seed=0)
+        a = (bf16(c.q), bf16(c.k), bf16(c.v), i32(c.cu_seqlens))
+        o = torch.empty_like(a[0])
+        lse = torch.empty((32, S), dtype=torch.float32, device=dev)
+
+        def f():
+            mi.attn_fwd(*a, c.max_seqlen, scale=c.scale, causal=True, out=o, lse=lse)
+        med, mn = timed(f, 50, True)
+        fl = accounting.prefill_flops(c.seqlens, 32, 128, True)
+        emit({"cell": f"config2 causal GQA prefill S={S}", "us_median": round(med, 2), "us_min": round(mn, 2),
+              "TFLOP/s": round(fl / med / 1e6, 1), "frac_mfma": round(fl / med / 1e6 / PEAK_BF16_TFLOPS, 4),
+              "flushed": True})
+        del a, o, lse
+
+    # config 3: paged decode, 64 sequences
+    c3 = synth.config3(seed=0, tail="zero")
+    a3 = (bf16(c3.q), bf16(c3.k_cache), bf16(c3.v_cache), i32(c3.block_table), i32(c3.seq_lens))
+    by3 = accounting.decode_bytes(c3.seq_lens, 32, 8, 128)
+    for S in (0, 1, 2, 4, 8, 16, 32):
+        med, mn = timed(lambda: mi.attn_decode_paged(*a3, scale=c3.scale, num_splits=S), 200, False)
+        emit({"cell": f"config3 paged decode B=64 splits={S or 'library plan'}", "us_median": round(med, 2),
+              "us_min": round(mn, 2), "GB/s": round(by3 / med / 1e3, 1),
+              "frac_hbm": round(by3 / med / 1e3 / PEAK_HBM_GBS, 4), "working_set_MB": round(by3 / 1e6, 1),
+              "flushed": False})
+    if oracle_too:
+        q, kc, vc = c3.as_f64()
+        emit({"cell": "config3 oracle", "oracle": oracle_time(
+            lambda: oracle.decode_dense(q, kc, vc, c3.block_table, c3.seq_lens, c3.scale), by3, "GB/s",
+            "whole workload (64 sequences, all heads)")})
+        del q, kc, vc
+    del a3
+
+    # config 4: long decode, contexts 16K-128K x split counts
+    for ctx in (16384, 32768, 65536, 131072):
+        c = synth.config4(ctx=ctx, seed=0)
+        a = (bf16(c.q), bf16(c.k_cache), bf16(c.v_cache), i32(c.block_table), i32(c.seq_lens))
+        by = accounting.decode_bytes(c.seq_lens, 16, 4, 256)
+        cold = by < 512e6
+        for S in (1, 16, 64, 256, 0):
+            med, mn = timed(lambda: mi.attn_decode_paged(*a, scale=c.scale, num_splits=S), 200, cold)
+            emit({"cell": f"config4 long decode ctx={ctx} splits={S or 'policy'}", "us_median": round(med, 2),
+                  "us_min": round(mn, 2), "GB/s": round(by / med / 1e3, 1),
+                  "frac_hbm": round(by / med / 1e3 / PEAK_HBM_GBS, 4), "working_set_MB": round(by / 1e6, 1),
+                  "flushed": cold})
+        if oracle_too and ctx == 131072:
+            q, kc, vc = c.as_f64()
+            emit({"cell": "config4 oracle ctx=131072", "oracle": oracle_time(
+                lambda: oracle.decode_dense(q, kc, vc, c.block_table, c.seq_lens, c.scale), by, "GB/s",
+                "whole workload (128K tokens, 16 heads)")})
+            del q, kc, vc
+        del a
+        torch.cuda.empty_cache()
+
+    # config 5: varlen causal prefill, head_dim 256
+    c5 = synth.config5(seed=0)
+    a5 = (bf16(c5.q), bf16(c5.k), bf16(c5.v), i32(c5.cu_seqlens))
+    o5 = torch.empty_like(a5[0])
+    l5 = torch.empty((16, c5.total_tokens), dtype=torch.float32, device=dev)
+    med, mn = timed(lambda: mi.attn_fwd(*a5, c5.max_seqlen, scale=c5.scale, causal=True, out=o5, lse=l5), 20,
+                    False)
+    fl5 = accounting.prefill_flops(c5.seqlens, 16, 256, True)
+    emit({"cell": "config5 varlen causal prefill D=256", "us_median": round(med, 2), "us_min": round(mn, 2),
+          "TFLOP/s": round(fl5 / med / 1e6, 1), "frac_mfma": round(fl5 / med / 1e6 / PEAK_BF16_TFLOPS, 4),
+          "flushed": False})
+    if oracle_too:
+        # the longest sequence alone (all 16 heads)
+        b = int(np.argmax(c5.seqlens))
+        s0, s1 = int(c5.cu_seqlens[b]), int(c5.cu_seqlens[b + 1])
+        q, k, v = c5.as_f64()
+        q, k, v = q[s0:s1], k[s0:s1], v[s0:s1]
+        emit({"cell": "config5 oracle", "oracle": oracle_time(
+            lambda: oracle.attention_dense(q, k, v, np.array([0, s1 - s0]), 16, 4, c5.scale, True),
+            accounting.prefill_flops([s1 - s0], 16, 256, True), "TFLOP/s",
+            f"the longest sequence ({s1 - s0} tokens), all 16 heads", min_s=1.0)})
+    del a5, o5, l5
 
 
 # kernels whose HBM traffic the counter summary records: key -> (stage run by
@@ -289,6 +478,12 @@ def main():
     ap.add_argument("--sweep-splits", action="store_true",
                     help="time paged decode over split counts on a grid of batch sizes and contexts and print "
                          "the library policy's pick beside the fastest (one JSON line per cell)")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="measure the matrix cores' sustained bf16 rate with a register-operand probe")
+    ap.add_argument("--cells", action="store_true",
+                    help="time every workload cell (one op per cell, per-call events, cache flush below 512 MB)")
+    ap.add_argument("--cells-oracle", action="store_true",
+                    help="with --cells: also time the fp64 oracle on a bounded sample of each workload")
     ap.add_argument("--numerics", action="store_true",
                     help="time the decode numerics variants beside the fast path (one JSON line each)")
     ap.add_argument("--summarize-counters", metavar="DIR", default=None,
@@ -315,8 +510,17 @@ def main():
     def i32(a):
         return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
 
+    def f32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
     if args.sweep_splits:
         sweep_splits(torch, mi, dev)
+        return
+    if args.mfma_peak:
+        mfma_peak(torch, dev)
+        return
+    if args.cells:
+        cells(torch, mi, dev, bf16, i32, f32, args.cells_oracle)
         return
 
     if args.numerics:
