@@ -112,8 +112,11 @@ void launch_fwd_c(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t s
 constexpr int fwd_qb(int d) { return d >= 256 ? 1 : 1; }
 
 // Dense prefill with head_dim 64 and 128 runs the eight-wave ping-pong kernel
-// (two 32-row groups per query tile); head_dim 256 and the paged (chunked)
-// prefill run the four-wave kernel, which measured faster there.
+// (two 32-row groups per query tile) when its grid has at least one
+// workgroup per compute unit; smaller problems, head_dim 256 and the paged
+// (chunked) prefill run the four-wave kernel, which measured faster there
+// (half the rows per workgroup: twice the workgroups, half the per-workgroup
+// critical path). Both kernels give the same bits.
 constexpr bool fwd_pingpong(int d, bool paged) { return d <= 128 && !paged; }
 
 template <int D, int KB, bool F16V>
@@ -129,14 +132,15 @@ void launch_fwd_pp(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t 
 // probabilities are rounded to fp16 instead of bf16.
 constexpr bool fwd_f16v(int d) { return d >= 256; }
 
-// bf16 prefill grid: (head slot, query-tile pair, sequence)
+// bf16 prefill grid: (head slot, query-tile pair, sequence); `pingpong`:
+// the eight-wave kernel's query tiles (twice the four-wave kernel's rows)
 long fwd_setup(miattn::FwdArgs& a, int num_seqs, int max_seqlen, int num_q_heads, int num_kv_heads, int head_dim,
-               bool unit_per_tile = false) {
+               bool pingpong, bool unit_per_tile = false) {
   const int G = num_q_heads / num_kv_heads;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
   a.heads_per_wg = G >= 4 ? 4 : G;
-  const int QR = 32 * fwd_qb(head_dim) * (4 / a.heads_per_wg) * (fwd_pingpong(head_dim, unit_per_tile) ? 2 : 1);
+  const int QR = 32 * fwd_qb(head_dim) * (4 / a.heads_per_wg) * (pingpong ? 2 : 1);
   const int n_qtiles = (max_seqlen + QR - 1) / QR;
   a.n_pairs = unit_per_tile ? n_qtiles : (n_qtiles + 1) / 2;
   a.n_head_slots = num_kv_heads * (G / a.heads_per_wg);
@@ -383,9 +387,9 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
     const long grid = (long)num_q_heads * num_seqs * a.n_qtiles;
     if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: problem too large");
     if (causal)
-      hipLaunchKernelGGL((miattn::miattn_prefill_fwd_f32_kernel<true>), dim3((unsigned)grid), dim3(64), 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_prefill_fwd_f32_kernel<true>), dim3((unsigned)grid), dim3(512), 0, st, a);
     else
-      hipLaunchKernelGGL((miattn::miattn_prefill_fwd_f32_kernel<false>), dim3((unsigned)grid), dim3(64), 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_prefill_fwd_f32_kernel<false>), dim3((unsigned)grid), dim3(512), 0, st, a);
     const int r = check_launch("prefill fp32");
     return r ? r : ok();
   }
@@ -396,7 +400,12 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
   a.total_tokens = total_tokens;
   a.c = c;
   a.seq_lens_k = nullptr; a.block_table = nullptr; a.max_pages = 0; a.num_pages = 0;
-  const long grid = fwd_setup(a, num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim);
+  bool pp = fwd_pingpong(head_dim, false);
+  long grid = fwd_setup(a, num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim, pp);
+  if (pp && grid < kCUs) {
+    pp = false;
+    grid = fwd_setup(a, num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim, pp);
+  }
   if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd: problem too large");
   const bool cz = causal != 0;
   if (fwd_f16v(head_dim)) {
@@ -411,16 +420,17 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
                        (const uint16_t*)v, (uint16_t*)ws, n8);
     a.v = (const uint16_t*)ws;
   }
+  static_assert(!fwd_f16v(64) && !fwd_f16v(128) && fwd_f16v(256), "P.V precision by head_dim");
   switch (head_dim) {
     case 64:
-      if (fwd_f16v(64)) launch_fwd_pp<64, 2, true>(a, (int)grid, cz, st);
-      else launch_fwd_pp<64, 2, false>(a, (int)grid, cz, st);
+      if (pp) launch_fwd_pp<64, 2, false>(a, (int)grid, cz, st);
+      else launch_fwd_c<64, fwd_qb(64), 2, false, false>(a, (int)grid, cz, st);
       break;
     case 128:
-      if (fwd_f16v(128)) launch_fwd_pp<128, 2, true>(a, (int)grid, cz, st);
-      else launch_fwd_pp<128, 2, false>(a, (int)grid, cz, st);
+      if (pp) launch_fwd_pp<128, 2, false>(a, (int)grid, cz, st);
+      else launch_fwd_c<128, fwd_qb(128), 2, false, false>(a, (int)grid, cz, st);
       break;
-    default: launch_fwd_c<256, fwd_qb(256), 1, false, fwd_f16v(256)>(a, (int)grid, cz, st); break;
+    default: launch_fwd_c<256, fwd_qb(256), 1, false, true>(a, (int)grid, cz, st); break;
   }
   const int r = check_launch("prefill bf16");
   return r ? r : ok();
@@ -460,7 +470,7 @@ int miattn_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cach
   a.c = scale * miattn::kLog2e;
   a.seq_lens_k = seq_lens_k; a.block_table = block_table;
   a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
-  const long grid = fwd_setup(a, num_seqs, max_seqlen_q, num_q_heads, num_kv_heads, head_dim, true);
+  const long grid = fwd_setup(a, num_seqs, max_seqlen_q, num_q_heads, num_kv_heads, head_dim, false, true);
   if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd_paged: problem too large");
   const bool cz = causal != 0;
   switch (head_dim) {

@@ -466,9 +466,18 @@ struct FwdF32Args {
   float c;
 };
 
+// fp32 prefill (head_dim 64): one workgroup of 8 waves per (query tile of
+// 32 rows, head, sequence). The key range is shared out over the waves, tile
+// kt to wave kt mod 8, each keeping its own running max, sum and output
+// (S^T = K Q^T and O^T += V^T P^T on 32x32x2 fp32 MFMAs, operands straight
+// from global memory); the 8 partial states are merged through LDS in wave
+// order, so a short sequence's latency is one eighth of its key tiles.
 template <bool CAUSAL>
-__global__ __launch_bounds__(64) void miattn_prefill_fwd_f32_kernel(FwdF32Args a) {
+__global__ __launch_bounds__(512) void miattn_prefill_fwd_f32_kernel(FwdF32Args a) {
   constexpr int D = 64;
+  constexpr int NW = 8;
+  __shared__ f32x4 part[NW][8][64];   // [wave][4-value chunk][lane]
+  __shared__ float pm[NW][32], pl[NW][32];
   const int lin = blockIdx.x;
   const int h = lin % a.num_q_heads;
   const int rest = lin / a.num_q_heads;
@@ -480,8 +489,9 @@ __global__ __launch_bounds__(64) void miattn_prefill_fwd_f32_kernel(FwdF32Args a
   s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
   const int L = s1 - s0;
   const int q0 = qt * 32;
-  if (q0 >= L) return;
-  const int lane = threadIdx.x;
+  if (q0 >= L) return;   // uniform over the workgroup
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int half = lane >> 5;
   const int qrow = q0 + (lane & 31);
   const int g = h / a.group;
@@ -504,7 +514,18 @@ __global__ __launch_bounds__(64) void miattn_prefill_fwd_f32_kernel(FwdF32Args a
   const float* kb = a.k + (size_t)s0 * kv_row + (size_t)g * D;
   const float* vb = a.v + (size_t)s0 * kv_row + (size_t)g * D;
 
-  for (int k0 = 0; k0 < kend; k0 += 32) {
+  for (int k0 = 32 * wave; k0 < kend; k0 += 32 * NW) {
+    // V operands of the tile, loaded first so their latency overlaps S:
+    // step r pairs key 8(r/4) + r%4 (lanes < 32) with key + 4
+    float vv[16][2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+      const bool ok = key < L;
+      const float* vp = vb + (size_t)(ok ? key : 0) * kv_row + (lane & 31);
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) vv[r][dt] = ok ? vp[32 * dt] : 0.f;
+    }
     // S^T (32 keys x 32 queries); A = K (row key k0 + lane%32, col d = 2 st + half)
     f32x16 s;
 #pragma unroll
@@ -536,32 +557,46 @@ __global__ __launch_bounds__(64) void miattn_prefill_fwd_f32_kernel(FwdF32Args a
       s[r] = exp2_hw(s[r] - mu);
       l += s[r];
     }
-    // O^T += V^T P^T, step r pairs key 8(r/4) + r%4 (lanes < 32) with key + 4
+    // O^T += V^T P^T
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
-      const bool ok = key < L;
-      const float* vp = vb + (size_t)(ok ? key : 0) * kv_row + (lane & 31);
+    for (int r = 0; r < 16; ++r)
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(ok ? vp[32 * dt] : 0.f, s[r], acc[dt], 0, 0, 0);
-    }
+      for (int dt = 0; dt < 2; ++dt) acc[dt] = __builtin_amdgcn_mfma_f32_32x32x2f32(vv[r][dt], s[r], acc[dt], 0, 0, 0);
   }
   l += xor32(l);
+
+  // merge: wave w combines value chunk w (row lane % 32, d = 32 (w / 4) +
+  // 8 (w % 4) + 4 half + 0..3) of the 8 partial states, in wave order
+  if (lane < 32) {
+    pm[wave][lane] = m;
+    pl[wave][lane] = l;
+  }
+#pragma unroll
+  for (int c = 0; c < 8; ++c) {
+    const f32x16& A = acc[c >> 2];
+    part[wave][c][lane] = (f32x4){A[4 * (c & 3)], A[4 * (c & 3) + 1], A[4 * (c & 3) + 2], A[4 * (c & 3) + 3]};
+  }
+  __syncthreads();
+  const int row = lane & 31;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) M = fmaxf(M, pm[w][row]);
+  float lt = 0.f;
+  f32x4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const float mw = pm[w][row];
+    const float f = (mw == kNegInf) ? 0.f : exp2_hw(mw - M);
+    lt += f * pl[w][row];
+    o += f * part[w][wave][lane];
+  }
   if (qrow < L) {
-    const bool empty = !(l > 0.f);
-    const float inv = empty ? 0.f : 1.f / l;
-    float* op = a.o + ((size_t)(s0 + qrow) * Hq + h) * D + 4 * half;
-#pragma unroll
-    for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4 w = {acc[dt][4 * r4] * inv, acc[dt][4 * r4 + 1] * inv, acc[dt][4 * r4 + 2] * inv,
-                   acc[dt][4 * r4 + 3] * inv};
-        *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * r4) = w;
-      }
-    if (a.lse != nullptr && half == 0)
-      a.lse[(size_t)h * a.total_tokens + s0 + qrow] = empty ? kNegInf : (m + log2_hw(l)) * kLn2;
+    const bool empty = !(lt > 0.f);
+    const float inv = empty ? 0.f : 1.f / lt;
+    float* op = a.o + ((size_t)(s0 + qrow) * Hq + h) * D + 32 * (wave >> 2) + 8 * (wave & 3) + 4 * half;
+    *reinterpret_cast<f32x4*>(op) = o * inv;
+    if (a.lse != nullptr && wave == 0 && half == 0)
+      a.lse[(size_t)h * a.total_tokens + s0 + qrow] = empty ? kNegInf : (M + log2_hw(lt)) * kLn2;
   }
 }
 

@@ -11,10 +11,12 @@ Bar for the given-input comparison: the bf16 bar of the forward (max-abs 1e-2,
 mean-abs 1e-3) on dQ, dK and dV, with the max-abs part applied to the error
 beyond each element's own rounding to bf16: gradients are unbounded sums
 (magnitudes up to ~9 here), and half a bf16 ulp is already 0.0156 from 4 up.
-Bar for the pipeline: mean-abs 1e-3 against both references. Its max error is
-printed, not bounded here: the GPU's O carries the forward's own error (held
-to the forward's bar by its tests), and the row term dO . O of the backward
-sums that error over the head dimension. Beyond parity: bitwise
+Bar for the pipeline: mean-abs 1e-3 against both references, and max-abs
+2e-2 on the error beyond each element's own bf16 rounding. The pipeline adds
+two error sources, each held to 1e-2 by its own bar: the backward's (the
+given-input comparison above) and the forward's output error, which enters
+through the stored O (the row term dO . O sums it over the head dimension);
+their sum is the pipeline's bound. Beyond parity: bitwise
 repeatability, and the closed forms the oracle is pinned with (the keys' dV
 sum to the queries' dO sum, the keys' dK sum to zero) on every head at the
 full 4096-token size.
@@ -29,7 +31,7 @@ import attention_attn_fwd_03_amd as mi
 import oracle
 import synth
 from gpu_util import assert_bf16_close_beyond_rounding as assert_grad_close
-from gpu_util import bf16_dev, bitwise_equal, errors, f32_dev, host, i32_dev
+from gpu_util import bf16_dev, bitwise_equal, errors, f32_dev, half_ulp_bf16, host, i32_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -89,8 +91,11 @@ def check(c, seed=0, pipeline=True):
         for what, want in (("given-form reference", ref), ("exact gradients", exact)):
             for name, g, w in zip(("dQ", "dK", "dV"), got, want):
                 mx, mean = errors(g, w)
-                print(f"  {c.name} pipeline vs {what} {name}: max-abs {mx:.3e} mean-abs {mean:.3e}", flush=True)
+                excess = float(np.max(np.abs(g - w) - half_ulp_bf16(w))) if g.size else 0.0
+                print(f"  {c.name} pipeline vs {what} {name}: max-abs {mx:.3e} (beyond rounding {excess:.3e}) "
+                      f"mean-abs {mean:.3e}", flush=True)
                 assert mean <= 1e-3, (what, name, mean)
+                assert excess <= 2e-2, (what, name, excess)
 
 
 @pytest.mark.parametrize("causal", [True, False])
