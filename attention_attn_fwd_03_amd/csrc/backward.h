@@ -21,7 +21,9 @@
 //    sums are added through LDS in a fixed order. Per tile: S = Q K^T and dP = dO V^T (query rows, key columns),
 //    then dV^T += dO^T P and dK^T += Q^T dS: the accumulator registers of P
 //    and dS, rounded to fp16, are the B operand as they stand; dO^T and Q^T
-//    come from the same LDS tile through the transposing read.
+//    come from the same LDS tile through the transposing read. At head_dim
+//    256 the four waves share each Q/dO tile and split 64 keys instead
+//    (miattn_bwd_dkdv_d256_kernel).
 //  * dQ: the forward's orientation: one wave per 32 query rows of one head,
 //    S^T = K Q^T and dP^T = V dO^T with Q, dO held as operands, K/V tiles
 //    streaming through LDS, dQ^T += K^T dS^T with K^T read transposed.
@@ -64,7 +66,7 @@ struct BwdArgs {
   int group;                  // G
   int heads_per_wg;           // dQ kernel: query heads per workgroup (NH)
   int n_head_slots;           // dQ kernel: Hkv * G / NH
-  int n_kblocks;              // dK/dV grid: 32-key blocks per sequence (ceil(max_seqlen / 32))
+  int n_kblocks;              // dK/dV grid: key blocks per sequence (32 keys; 64 at head_dim 256)
   int n_qunits;               // dQ grid: query tiles per sequence
   float c;                    // scale * log2(e)
   float scale;
@@ -431,11 +433,261 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- dK / dV, head_dim 256
+// At head_dim 256 the form above does not fit: each wave's double-buffered
+// 32-row Q and dO tiles are 16 KB apiece (256 KB of LDS for four waves), and
+// dK^T, dV^T of 32 keys take 256 accumulator registers. Here the four waves of
+// a workgroup share one double-buffered Q/dO tile and split the workgroup's 64
+// keys, 16 each, on 16x16x32 MFMAs: dK^T and dV^T of 16 keys are 16 blocks of
+// 16 x 16 each (128 registers), the 16 keys' K and V operands stay in
+// registers, and every (query head, 32-query tile) step of the group is taken
+// by all four waves between two workgroup barriers. Each key belongs to one
+// wave, so the sums need no merge across waves.
+// Lane l (c = l mod 16, j = l / 16) in the 16x16x32 products: A holds row c and
+// k-elements 8j..8j+7, B column c and the same k-elements, the result column c
+// and rows 4j..4j+3. With k over the 32 queries of a tile, element m of a
+// lane's eight stands for query 16 (m / 4) + 4j + m mod 4, which is where the
+// two 16-query blocks of S leave a lane's P values; the dO^T and Q^T operands
+// read the same queries through the transposing LDS read.
+template <bool CAUSAL>
+__global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_d256_kernel(BwdArgs a) {
+  constexpr int D = 256;
+  using TL = BwdTile<D>;
+  constexpr int CH = TL::CH;                         // 16-byte chunks per row
+  constexpr int QT = 32;                             // queries per tile
+  constexpr int KW = 16;                             // keys per wave
+  constexpr int TILE = QT * D * 2;                   // bytes of one Q or dO tile
+  constexpr int NC = TILE / 1024;                    // 1-KB copies per tensor and tile
+  constexpr int NCW = NC / 4;                        // ... issued by each wave
+  constexpr int NKS = D / 32;                        // 16x16x32 steps over the head dim
+  constexpr int NDB = D / 16;                        // 16-row blocks of dK^T / dV^T
+  static_assert(NC % 4 == 0, "copies must split over the four waves");
+  // separate LDS objects per buffer, as in the kernel above
+  __shared__ __attribute__((aligned(1024))) uint8_t q_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t q_lds1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t d_lds0[TILE];
+  __shared__ __attribute__((aligned(1024))) uint8_t d_lds1[TILE];
+  __shared__ __attribute__((aligned(16))) float st_lds0[64];   // 32 LSE, 32 Delta
+  __shared__ __attribute__((aligned(16))) float st_lds1[64];
+
+  // work item: (kv head, 64-key block, sequence), kv head fastest, sequence
+  // slowest; key block 0 (the most causal work) first
+  const int lin = blockIdx.x;
+  const int g = lin % a.num_kv_heads;
+  const int rest = lin / a.num_kv_heads;
+  const int kblk = rest % a.n_kblocks;
+  const int b = rest / a.n_kblocks;
+  int s0 = a.cu_seqlens[b];
+  int s1 = a.cu_seqlens[b + 1];
+  s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
+  s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
+  const int L = s1 - s0;
+  const int kb0 = kblk * 4 * KW;
+  if (kb0 >= L) return;   // uniform over the workgroup
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15, j4 = lane >> 4;
+  const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = a.group;
+  const float c = a.c;
+  const int kw0 = kb0 + KW * wave;                   // this wave's first key
+  const int key = kw0 + c16;                         // this lane's key column
+  const bool key_ok = key < L;
+  const bool wave_live = kw0 < L;
+
+  const uint32_t qaddr0 = (uint32_t)(uintptr_t)(MIATTN_LDS uint8_t*)q_lds0;
+  const uint32_t qaddr1 = (uint32_t)(uintptr_t)(MIATTN_LDS uint8_t*)q_lds1;
+  const uint32_t daddr0 = (uint32_t)(uintptr_t)(MIATTN_LDS uint8_t*)d_lds0;
+  const uint32_t daddr1 = (uint32_t)(uintptr_t)(MIATTN_LDS uint8_t*)d_lds1;
+  const uint32_t saddr0 = (uint32_t)(uintptr_t)(MIATTN_LDS float*)st_lds0;
+  const uint32_t saddr1 = (uint32_t)(uintptr_t)(MIATTN_LDS float*)st_lds1;
+
+  // K and V of this lane's key as B operands (fp16 copies): d = 32 ks + 8 j4
+  // .. + 7; keys past the sequence end repeat its last key (masked below)
+  u32x4 kreg[NKS], vreg[NKS];
+  {
+    const int kr = key_ok ? key : L - 1;
+    const size_t off = ((size_t)(s0 + kr) * Hkv + g) * D + 8 * j4;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      kreg[ks] = ld16(a.k16 + off + 32 * ks);
+      vreg[ks] = ld16(a.v16 + off + 32 * ks);
+    }
+  }
+
+  // steps: (query head of the group, query tile), causal tiles from the one
+  // holding query kb0; all four waves take every step
+  const int n_qt = (L + QT - 1) / QT;
+  const int qt0 = CAUSAL ? kb0 / QT : 0;
+  const int nq = n_qt - qt0;
+  const int n_steps = G * nq;
+
+  // copy j of a tile (this wave's NCW of the NC): lane fills slot lidx % CH of
+  // row lidx / CH (lidx = 64 j + lane) with the chunk the swizzle maps there;
+  // rows past the sequence end repeat its last row (their P and dS are 0)
+  const size_t q_row = (size_t)Hq * D;
+  uint32_t qoff[NCW];
+#pragma unroll
+  for (int jj = 0; jj < NCW; ++jj) {
+    const int lidx = (wave * NCW + jj) * 64 + lane;
+    const int r = lidx / CH;
+    const int slot = lidx % CH;
+    qoff[jj] = (uint32_t)(((size_t)r * q_row + 8 * (slot ^ TL::swz(r))) * 2);
+  }
+  const uint32_t st_lane = (uint32_t)(((lane >= 8 ? (size_t)Hq * a.t_pad : 0) + 4 * (lane & 7)) * 4);
+  auto load_tile = [&](int st, int buf) {
+    const int h = g * G + st / nq;
+    const int q0 = (qt0 + st % nq) * QT;
+    const bool full = q0 + QT <= L;
+    const char* qsrc = (const char*)(a.q16 + ((size_t)(s0 + q0) * Hq + h) * D);
+    const char* dsrc = (const char*)(a.do16 + ((size_t)(s0 + q0) * Hq + h) * D);
+#pragma unroll
+    for (int jj = 0; jj < NCW; ++jj) {
+      uint32_t off = qoff[jj];
+      if (!full) {
+        const int r = ((wave * NCW + jj) * 64 + lane) / CH;
+        const int rr = q0 + r < L ? r : L - 1 - q0;
+        off -= (uint32_t)((size_t)(r - rr) * q_row * 2);
+      }
+      const uint32_t lo = (uint32_t)((wave * NCW + jj) * 1024);
+      dma16_to_lds_asm(qsrc, off, (buf ? qaddr1 : qaddr0) + lo);
+      dma16_to_lds_asm(dsrc, off, (buf ? daddr1 : daddr0) + lo);
+    }
+    if (wave == 0 && lane < 16)
+      dma16_to_lds_asm(a.stats, st_lane + (uint32_t)(((size_t)h * a.t_pad + s0 + q0) * 4), buf ? saddr1 : saddr0);
+  };
+
+  f32x4 dk_acc[NDB], dv_acc[NDB];
+#pragma unroll
+  for (int i = 0; i < NDB; ++i)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      dk_acc[i][r] = 0.f;
+      dv_acc[i][r] = 0.f;
+    }
+
+  if (n_steps > 0) load_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  for (int i = 0; i < n_steps; ++i) {
+    const int buf = i & 1;
+    if (i + 1 < n_steps) load_tile(i + 1, buf ^ 1);
+    const int q0 = (qt0 + i % nq) * QT;
+    // a causal step whose queries all precede this wave's keys adds nothing
+    if (wave_live && (!CAUSAL || q0 + QT - 1 >= kw0)) {
+      const MIATTN_LDS uint8_t* ql = (const MIATTN_LDS uint8_t*)(uintptr_t)(buf ? qaddr1 : qaddr0);
+      const MIATTN_LDS uint8_t* dl_ = (const MIATTN_LDS uint8_t*)(uintptr_t)(buf ? daddr1 : daddr0);
+      const MIATTN_LDS float* sl = (const MIATTN_LDS float*)(uintptr_t)(buf ? saddr1 : saddr0);
+      // S = Q K^T and dP = dO V^T for the two 16-query blocks: A = query row
+      // 16 qb + c16, chunk 4 ks + j4
+      f32x4 s[2], dp[2];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        dp[qb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        const int r = 16 * qb + c16;
+        auto so = [&](int ks) { return r * (2 * D) + 16 * ((4 * ks + j4) ^ TL::swz(r)); };
+        u32x4 oq = lds_ld16(ql + so(0)), od = lds_ld16(dl_ + so(0));
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) {
+          u32x4 nq_ = oq, nd = od;
+          if (ks + 1 < NKS) {
+            nq_ = lds_ld16(ql + so(ks + 1));
+            nd = lds_ld16(dl_ + so(ks + 1));
+          }
+          s[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(oq), as_f16x8(kreg[ks]), s[qb], 0, 0, 0);
+          dp[qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(od), as_f16x8(vreg[ks]), dp[qb], 0, 0, 0);
+          oq = nq_; od = nd;
+        }
+      }
+      // this lane's rows 16 qb + 4 j4 + e: LSE (log2) and Delta
+      float l2[2][4], dl[2][4];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const f32x4 lv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sl + 16 * qb + 4 * j4);
+        const f32x4 dv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sl + 32 + 16 * qb + 4 * j4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          l2[qb][e] = lv[e];
+          dl[qb][e] = dv[e];
+        }
+      }
+      // the mask on the exponential's inputs, on tail and diagonal steps only
+      const bool need_mask = kw0 + KW > L || q0 + QT > L || (CAUSAL && kw0 + KW - 1 > q0);
+      if (need_mask) {
+        asm volatile("" ::: "memory");   // keep this a branch: the common step skips it
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int qrow = q0 + 16 * qb + 4 * j4 + e;
+            const bool ok = key_ok & (qrow < L) & (!CAUSAL | (key <= qrow));
+            s[qb][e] = ok ? s[qb][e] : kNegInf;
+            l2[qb][e] = ok ? l2[qb][e] : 0.f;
+            dl[qb][e] = ok ? dl[qb][e] : 0.f;
+          }
+      }
+      u32x4 pw, dsw;
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        float p[4], d[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          p[e] = exp2_hw(__builtin_fmaf(s[qb][e], c, -l2[qb][e]));
+          d[e] = p[e] * (dp[qb][e] - dl[qb][e]);
+        }
+        pw[2 * qb] = pack_f16x2(p[0], p[1]);
+        pw[2 * qb + 1] = pack_f16x2(p[2], p[3]);
+        dsw[2 * qb] = pack_f16x2(d[0], d[1]);
+        dsw[2 * qb + 1] = pack_f16x2(d[2], d[3]);
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS: block j4 of 16 lanes reads query
+      // rows 4 j4 + {0..3} and 16 + 4 j4 + {0..3}, head-dim columns
+      // 16 db + {0..15}, through the transposing read
+      const int r0 = 4 * j4 + (c16 >> 2);
+      const int r1 = r0 + 16;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = 16 * db + 4 * (c16 & 3);
+        const int ch = col >> 3, sub = (col & 7) * 2;
+        const int o0 = r0 * (2 * D) + 16 * (ch ^ TL::swz(r0)) + sub;
+        const int o1 = r1 * (2 * D) + 16 * (ch ^ TL::swz(r1)) + sub;
+        const f16x8 dot = as_f16x8(lds_ld_tr16(dl_ + o0), lds_ld_tr16(dl_ + o1));
+        const f16x8 qtr = as_f16x8(lds_ld_tr16(ql + o0), lds_ld_tr16(ql + o1));
+        dv_acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(dot, as_f16x8(pw), dv_acc[db], 0, 0, 0);
+        dk_acc[db] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qtr, as_f16x8(dsw), dk_acc[db], 0, 0, 0);
+      }
+    }
+    // the next step's copies (every wave's) have landed, and no wave still
+    // reads the buffer the step after will fill
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+
+  // lane: key kw0 + c16, head-dim columns 16 db + 4 j4 .. + 3 of block db
+  if (key_ok) {
+    const size_t go = ((size_t)(s0 + key) * Hkv + g) * D + 4 * j4;
+    const float sc = a.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const f32x4 kv = dk_acc[db] * sc;
+      const f32x4 vv = dv_acc[db];
+      u32x2 wk = {pack_bf16x2(kv[0], kv[1]), pack_bf16x2(kv[2], kv[3])};
+      u32x2 wv = {pack_bf16x2(vv[0], vv[1]), pack_bf16x2(vv[2], vv[3])};
+      *reinterpret_cast<u32x2*>(a.dk + go + 16 * db) = wk;
+      *reinterpret_cast<u32x2*>(a.dv + go + 16 * db) = wv;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- dQ
-// Workgroup = 4 waves over NH = min(G, 4) query heads of one kv head and 4/NH
+// Workgroup = 4 waves over NH (the largest of 4, 2, 1 dividing G) query heads of one kv head and 4/NH
 // blocks of 32 query rows; K/V tiles of 32 KB keys are shared by the waves.
+// At head_dim 256 (KB = 1) Q and dO as operands and dQ^T take 256 registers,
+// so one workgroup runs per CU.
 template <int D, int KB, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void miattn_bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, D >= 256 ? 1 : 2) void miattn_bwd_dq_kernel(BwdArgs a) {
   using TL = BwdTile<D>;
   constexpr int CH = TL::CH;
   constexpr int BC = 32 * KB;

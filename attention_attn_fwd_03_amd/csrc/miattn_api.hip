@@ -132,6 +132,12 @@ void launch_fwd_pp(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t 
 // probabilities are rounded to fp16 instead of bf16.
 constexpr bool fwd_f16v(int d) { return d >= 256; }
 
+// Query heads of one kv-head group that a prefill workgroup serves together
+// (they share every K/V tile it loads): the largest of 4, 2, 1 dividing the
+// group size G, so any G runs; the G / NH workgroups of a group read the same
+// tiles, the second and later from L2.
+int fwd_heads_per_wg(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+
 // bf16 prefill grid: (head slot, query-tile pair, sequence); `pingpong`:
 // the eight-wave kernel's query tiles (twice the four-wave kernel's rows)
 long fwd_setup(miattn::FwdArgs& a, int num_seqs, int max_seqlen, int num_q_heads, int num_kv_heads, int head_dim,
@@ -139,7 +145,7 @@ long fwd_setup(miattn::FwdArgs& a, int num_seqs, int max_seqlen, int num_q_heads
   const int G = num_q_heads / num_kv_heads;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
-  a.heads_per_wg = G >= 4 ? 4 : G;
+  a.heads_per_wg = fwd_heads_per_wg(G);
   const int QR = 32 * fwd_qb(head_dim) * (4 / a.heads_per_wg) * (pingpong ? 2 : 1);
   const int n_qtiles = (max_seqlen + QR - 1) / QR;
   a.n_pairs = unit_per_tile ? n_qtiles : (n_qtiles + 1) / 2;
@@ -367,8 +373,6 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
   if (dtype == MIATTN_BF16) {
     if (head_dim != 64 && head_dim != 128 && head_dim != 256)
       return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd: bf16 head_dim must be 64, 128 or 256");
-    if (!(G == 1 || G == 2 || G % 4 == 0))
-      return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd: Hq/Hkv must be 1, 2 or a multiple of 4");
   } else if (head_dim != 64) {
     return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd: fp32 head_dim must be 64");
   }
@@ -458,8 +462,6 @@ int miattn_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cach
   if (head_dim != 64 && head_dim != 128 && head_dim != 256)
     return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd_paged: head_dim must be 64, 128 or 256");
   const int G = num_q_heads / num_kv_heads;
-  if (!(G == 1 || G == 2 || G % 4 == 0))
-    return fail(MIATTN_ERR_UNSUPPORTED, "attn_fwd_paged: Hq/Hkv must be 1, 2 or a multiple of 4");
   const int dev = current_device();
   if (dev < 0) return dev;
   hipStream_t st = (hipStream_t)stream;
@@ -661,10 +663,9 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
     return fail(MIATTN_ERR_INVALID_ARG, "%s: need Hq > 0, Hkv > 0 and Hq %% Hkv == 0", who);
   if (causal != 0 && causal != 1) return fail(MIATTN_ERR_INVALID_ARG, "%s: causal must be 0 or 1", who);
   if (!scale_ok(scale)) return fail(MIATTN_ERR_INVALID_ARG, "%s: scale must be finite and > 0", who);
-  if (head_dim != 64 && head_dim != 128) return fail(MIATTN_ERR_UNSUPPORTED, "%s: head_dim must be 64 or 128", who);
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(MIATTN_ERR_UNSUPPORTED, "%s: head_dim must be 64, 128 or 256", who);
   const int G = num_q_heads / num_kv_heads;
-  if (!(G == 1 || G == 2 || G % 4 == 0))
-    return fail(MIATTN_ERR_UNSUPPORTED, "%s: Hq/Hkv must be 1, 2 or a multiple of 4", who);
   if ((long)total_tokens * num_q_heads * head_dim > 0x7fffffffL ||
       2L * num_q_heads * bwd_t_pad(total_tokens) > 0x3fffffffL)
     return fail(MIATTN_ERR_INVALID_ARG, "%s: tensors above 2^31 elements are not supported", who);
@@ -694,14 +695,15 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
   a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
   a.cu_seqlens = cu_seqlens; a.num_seqs = num_seqs; a.total_tokens = total_tokens; a.t_pad = (int)t_pad;
   a.num_q_heads = num_q_heads; a.num_kv_heads = num_kv_heads; a.group = G;
-  a.heads_per_wg = G >= 4 ? 4 : G;
+  a.heads_per_wg = fwd_heads_per_wg(G);
   a.n_head_slots = num_kv_heads * (G / a.heads_per_wg);
   a.c = scale * miattn::kLog2e;
   a.scale = scale;
   const long rows = (long)total_tokens * (num_q_heads + num_kv_heads);
   const int rpb = 256 / (head_dim / 8);
   const unsigned g_prep = (unsigned)((rows + rpb - 1) / rpb);
-  a.n_kblocks = (max_seqlen + 31) / 32;
+  // head_dim 256: 64-key blocks (four waves of 16 keys)
+  a.n_kblocks = head_dim == 256 ? (max_seqlen + 63) / 64 : (max_seqlen + 31) / 32;
   const unsigned g_dkdv = (unsigned)((long)num_kv_heads * a.n_kblocks * num_seqs);
   const int QR = 32 * (4 / a.heads_per_wg);
   a.n_qunits = (max_seqlen + QR - 1) / QR;
@@ -716,7 +718,7 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
       hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<64, false>), dim3(g_dkdv), blk, 0, st, a);
       hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<64, 2, false>), dim3(g_dq), blk, 0, st, a);
     }
-  } else {
+  } else if (head_dim == 128) {
     hipLaunchKernelGGL(miattn::miattn_bwd_prep_kernel<128>, dim3(g_prep), blk, 0, st, a);
     if (causal) {
       hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<128, true>), dim3(g_dkdv), blk, 0, st, a);
@@ -724,6 +726,15 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
     } else {
       hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<128, false>), dim3(g_dkdv), blk, 0, st, a);
       hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<128, 2, false>), dim3(g_dq), blk, 0, st, a);
+    }
+  } else {
+    hipLaunchKernelGGL(miattn::miattn_bwd_prep_kernel<256>, dim3(g_prep), blk, 0, st, a);
+    if (causal) {
+      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_d256_kernel<true>), dim3(g_dkdv), blk, 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<256, 1, true>), dim3(g_dq), blk, 0, st, a);
+    } else {
+      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_d256_kernel<false>), dim3(g_dkdv), blk, 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<256, 1, false>), dim3(g_dq), blk, 0, st, a);
     }
   }
   const int r = check_launch(who);

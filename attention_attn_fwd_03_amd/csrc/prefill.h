@@ -8,7 +8,7 @@
 //
 // MI355X mapping:
 //  * Workgroup = 4 waves, one per SIMD. Waves split the NH query heads of one
-//    kv-head group (NH = min(G, 4)) and 4/NH row ranges; each wave owns QB
+//    kv-head group (NH: the largest of 4, 2, 1 dividing G) and 4/NH row ranges; each wave owns QB
 //    blocks of 32 query rows (64 rows for head_dim <= 128), so every K and V
 //    operand read from LDS feeds QB MFMAs (LDS bytes per flop halve at QB=2)
 //    and all waves reuse the same K/V tile (GQA sharing of "GPU Datapath",

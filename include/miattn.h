@@ -85,7 +85,7 @@ extern "C" {
  *   causal: 0 = every key of the sequence; 1 = key j <= query i (positions
  *        counted from each sequence's start; queries and keys coincide).
  *   dtype: MIATTN_BF16 with head_dim 64, 128 or 256, or MIATTN_FP32 with
- *        head_dim 64. bf16 inputs are multiplied on bf16 MFMA with fp32
+ *        head_dim 64; any Hq/Hkv. bf16 inputs are multiplied on bf16 MFMA with fp32
  *        accumulation; softmax state is fp32; O is rounded to bf16 once at
  *        the end; the row sums add the unrounded fp32 probabilities. In the
  *        P.V product the probabilities enter rounded to bf16 at head_dim 64
@@ -122,8 +122,8 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
  *   causal: 0 = every query sees all Lk keys; 1 = query i (0-based within the
  *            chunk) sees keys j <= i + Lk - Lq (queries aligned to the end of
  *            the sequence). A query that sees no key gets O = 0, LSE = -inf.
- *   page_size must be MIATTN_PAGE_SIZE; head_dim 64, 128 or 256; Hq/Hkv 1, 2
- *   or a multiple of 4. Numerics as miattn_attn_fwd with bf16.
+ *   page_size must be MIATTN_PAGE_SIZE; head_dim 64, 128 or 256; any Hq/Hkv.
+ *   Numerics as miattn_attn_fwd with bf16.
  *   num_seqs, max_seqlen_q, total_q, max_pages_per_seq, num_pages: host
  *   integers that size the grid and bound the indices.
  * Robustness: Lk is clamped to [0, max_pages_per_seq * 16]; block-table
@@ -309,8 +309,7 @@ size_t miattn_decode_numerics_workspace_bytes(int batch, int num_q_heads, int he
  *   q, k, v (o likewise); cu_seqlens, num_seqs, max_seqlen, scale, causal as
  *   for miattn_attn_fwd.
  *   dq [total_tokens, Hq, D], dk, dv [total_tokens, Hkv, D] bf16 (written).
- *   head_dim 64 or 128; Hq/Hkv 1, 2 or a multiple of 4 (MIATTN_ERR_UNSUPPORTED
- *   otherwise).
+ *   head_dim 64, 128 or 256 (MIATTN_ERR_UNSUPPORTED otherwise); any Hq/Hkv.
  *   workspace: miattn_attn_bwd_workspace_bytes bytes of device scratch (row
  *   terms and fp16 copies of the inputs), or NULL for the library-owned
  *   buffer of the stream. Inputs must lie inside fp16's range (|x| <= 65504): the products

@@ -70,7 +70,6 @@ def _dec(**kw):
     (dict(D=96), mi.ERR_UNSUPPORTED),
     (dict(dtype=7), mi.ERR_UNSUPPORTED),
     (dict(dtype=1, D=128), mi.ERR_UNSUPPORTED),
-    (dict(Hq=12, Hkv=4), mi.ERR_UNSUPPORTED),
 ])
 def test_fwd_validation(kw, code):
     assert _fwd(**kw) == code
@@ -103,7 +102,6 @@ def _fwdp(**kw):
     (dict(npg=0), mi.ERR_INVALID_ARG),
     (dict(ps=32), mi.ERR_UNSUPPORTED),
     (dict(D=96), mi.ERR_UNSUPPORTED),
-    (dict(Hq=12, Hkv=4), mi.ERR_UNSUPPORTED),
     (dict(Hq=6, Hkv=4), mi.ERR_INVALID_ARG),
     (dict(causal=3), mi.ERR_INVALID_ARG),
     (dict(scale=0.0), mi.ERR_INVALID_ARG),
@@ -302,9 +300,8 @@ def _bwd(**kw):
     (dict(Hq=6, Hkv=4), mi.ERR_INVALID_ARG),
     (dict(causal=2), mi.ERR_INVALID_ARG),
     (dict(scale=float("nan")), mi.ERR_INVALID_ARG),
-    (dict(D=256), mi.ERR_UNSUPPORTED),
+    (dict(D=512), mi.ERR_UNSUPPORTED),
     (dict(D=96), mi.ERR_UNSUPPORTED),
-    (dict(Hq=6, Hkv=2), mi.ERR_UNSUPPORTED),
     (dict(ws=1, wsb=16), mi.ERR_WORKSPACE),
 ])
 def test_bwd_validation(kw, code):

@@ -99,7 +99,9 @@ def check(c, seed=0, pipeline=True):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 8, 8), (128, 8, 4), (128, 4, 2), (64, 16, 2)])
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 8, 8), (128, 8, 4), (128, 4, 2), (64, 16, 2),
+                                      (128, 24, 8), (64, 12, 2), (128, 5, 1),    # G = 3, 6, 5 too
+                                      (256, 16, 4), (256, 4, 4), (256, 6, 2)])   # head_dim 256
 def test_small_varlen(D, Hq, Hkv, causal):
     # ragged lengths: a single token, tiles of 32 / 128 plus tails, several blocks
     lens = [1, 33, 128, 200, 7, 300]
@@ -119,6 +121,26 @@ def test_causal_gqa_4096():
     # the 4096-token causal GQA geometry (G = 4, D = 128) on 8 query heads so
     # the fp64 oracle stays quick
     check(synth.make_prefill(2, 1, [4096], 8, 2, 128, 1.0 / math.sqrt(128.0), True, "bf16", "bwd_causal_s4096"))
+
+
+def test_varlen_d256():
+    # the head_dim-256 varlen geometry (Hq = 16, Hkv = 4, scale 2^-4): packed
+    # causal sequences spanning many 64-key blocks and 32-query tiles
+    check(synth.make_prefill(5, 3, [700, 1, 1500, 2300], 16, 4, 256, 2.0 ** -4, True, "bf16", "bwd_varlen_d256"))
+
+
+def test_d256_repeatable_and_overestimate_bitwise():
+    c = synth.make_prefill(5, 4, [300, 64, 777], 8, 2, 256, 2.0 ** -4, True, "bf16", "bwd_d256_rep")
+    dout = synth.output_gradient(9, 4, c.total_tokens, c.num_q_heads, c.head_dim)
+    q, k, v, cu = bf16_dev(c.q), bf16_dev(c.k), bf16_dev(c.v), i32_dev(c.cu_seqlens)
+    o, lse = mi.attn_fwd(q, k, v, cu, max_len(c), scale=c.scale, causal=True)
+    do = bf16_dev(dout)
+    a = mi.attn_bwd(q, k, v, o, lse, do, cu, max_len(c), scale=c.scale, causal=True)
+    b = mi.attn_bwd(q, k, v, o, lse, do, cu, max_len(c), scale=c.scale, causal=True)
+    d = mi.attn_bwd(q, k, v, o, lse, do, cu, 2 * max_len(c) + 9, scale=c.scale, causal=True)
+    torch.cuda.synchronize()
+    for x, y, z in zip(a, b, d):
+        assert bitwise_equal(x, y) and bitwise_equal(x, z)
 
 
 def test_closed_forms_on_every_head_at_4096():

@@ -29,7 +29,7 @@ def pingpong_max_seqlen(case):
     workgroup per compute unit, so the library runs the eight-wave kernel
     rather than the four-wave one it takes for small grids."""
     G = case.num_q_heads // case.num_kv_heads
-    nh = min(G, 4)
+    nh = 4 if G % 4 == 0 else (2 if G % 2 == 0 else 1)
     slots = case.num_kv_heads * (G // nh)
     rows = 64 * (4 // nh)
     n = len(case.cu_seqlens) - 1
@@ -115,6 +115,14 @@ def test_varlen_d256_full_size_every_row():
     ([1000, 513], 8, 8, 128, True),  # G = 1: 256-row tiles, two-pass and single (middle) work items
     ([700, 3], 8, 4, 128, False),    # G = 2 non-causal, two passes and a ragged tail
     ([600, 5], 16, 2, 128, False),   # G = 8 non-causal
+    # group sizes that are neither 1, 2 nor a multiple of 4: one (G = 3, 5,
+    # 7) or two (G = 6) query heads per workgroup
+    ([300, 41], 24, 8, 128, True),   # G = 3, the 24:8 head layout
+    ([257], 6, 2, 64, False),        # G = 3, D = 64 non-causal
+    ([190, 1], 10, 2, 128, True),    # G = 5
+    ([500], 12, 2, 128, True),       # G = 6
+    ([129, 64], 7, 1, 256, True),    # G = 7, D = 256
+    ([100], 12, 1, 64, False),       # G = 12
 ])
 def test_shapes(lens, Hq, Hkv, D, causal):
     full_check(synth.make_prefill(20, 0, lens, Hq, Hkv, D, 1 / math.sqrt(D), causal, "bf16",

@@ -40,7 +40,8 @@ def check(c, causal=True):
 
 
 @pytest.mark.parametrize("causal", [True, False])
-@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 8, 8), (256, 16, 4), (128, 8, 4), (128, 16, 2)])
+@pytest.mark.parametrize("D,Hq,Hkv", [(128, 32, 8), (64, 8, 8), (256, 16, 4), (128, 8, 4), (128, 16, 2),
+                                      (128, 24, 8), (64, 12, 2)])   # G = 3 and 6 as well
 def test_chunks_against_oracle(D, Hq, Hkv, causal):
     # prefixes crossing the 64-page block-table window, a chunk longer than a
     # prefix, ragged chunk and cache ends, a one-token chunk
