@@ -387,7 +387,16 @@ def cells(torch, mi, dev, bf16, i32, f32, oracle_too: bool):
             lambda: oracle.attention_dense(q, k, v, np.array([0, s1 - s0]), 16, 4, c5.scale, True),
             accounting.prefill_flops([s1 - s0], 16, 256, True), "TFLOP/s",
             f"the longest sequence ({s1 - s0} tokens), all 16 heads", min_s=1.0)})
-    del a5, o5, l5
+    # the backward of the same varlen head_dim-256 problem (forward outputs once)
+    mi.attn_fwd(*a5, c5.max_seqlen, scale=c5.scale, causal=True, out=o5, lse=l5)
+    do5 = bf16(synth.output_gradient(9, 0, c5.total_tokens, 16, 256))
+    med, mn = timed(lambda: mi.attn_bwd(a5[0], a5[1], a5[2], o5, l5, do5, a5[3], c5.max_seqlen, scale=c5.scale,
+                                        causal=True), 10, False)
+    fb5 = accounting.backward_flops(c5.seqlens, 16, 256, True)
+    emit({"cell": "config5 varlen causal backward D=256", "us_median": round(med, 2), "us_min": round(mn, 2),
+          "TFLOP/s": round(fb5 / med / 1e6, 1), "frac_mfma": round(fb5 / med / 1e6 / PEAK_BF16_TFLOPS, 4),
+          "flushed": False})
+    del a5, o5, l5, do5
 
 
 # kernels whose HBM traffic the counter summary records: key -> (stage run by
