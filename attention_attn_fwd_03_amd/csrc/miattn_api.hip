@@ -288,7 +288,7 @@ constexpr int kCUs = 256;
 // Smallest batch x block-table width (in tokens) for which num_splits == 0
 // uses the length-proportional plan: measured, the plan's per-workgroup
 // start-up costs 1.5-3.7 us, which only launches of this size repay.
-constexpr long kDecodePlanMinTokens = 1L << 18;
+constexpr long kDecodePlanMinTokens = 1L << 17;
 constexpr int kDecodeWgPerCu = 1;
 constexpr int kMaxSplits = 256;
 constexpr double kPagesRuleThreshold = 0.85;

@@ -88,7 +88,7 @@ def sweep_splits(torch, mi, dev):
     """Paged decode time for split counts 1, 2, 4, ..., 256 and for the
     library's own plan (num_splits = 0) on synthetic caches (seeded
     device-side normals, shuffled 16-token pages), for the two decode shapes
-    and batch 1-64, contexts 1K-64K (fixed, and uniform in [ctx/8, ctx])."""
+    and batch 1-128, contexts 1K-64K (fixed, and uniform in [ctx/8, ctx])."""
     import statistics
     g = torch.Generator(device=dev)
     g.manual_seed(0)
@@ -130,31 +130,33 @@ def sweep_splits(torch, mi, dev):
         torch.cuda.synchronize()
         return statistics.median([a.elapsed_time(b) * 1e3 for a, b in evs])
 
+    # the grid of batch x context, plus launches around the plan's size
+    # threshold (batch x table width between 2^16 and 2^19 tokens)
+    grid = [(B, ctx) for B in (1, 4, 16, 64) for ctx in (1024, 4096, 16384, 65536) if B * ctx <= 1 << 20]
+    grid += [(8, 16384), (8, 32768), (16, 8192), (32, 4096), (32, 8192), (64, 2048), (64, 3072), (128, 2048)]
     for Hq, Hkv, D in ((32, 8, 128), (16, 4, 256)):
-        for B in (1, 4, 16, 64):
-            for ctx in (1024, 4096, 16384, 65536):
-                if B * ctx > 1 << 20:
+        for B, ctx in grid:
+            for var in (False, True):
+                if var and B == 1:
                     continue
-                for var in (False, True):
-                    if var and B == 1:
-                        continue
-                    lens = [ctx] * B if not var else [int(x) for x in torch.randint(ctx // 8, ctx + 1, (B,),
-                                                                                        generator=rng)]
-                    args = make(lens, Hq, Hkv, D)
-                    pol = mi.decode_pick_splits(B, Hkv, max(lens))
-                    cand = sorted({1, 2, 4, 8, 16, 32, 64, 128, 256, pol})
-                    res = {S: round(time_it(args, S, D ** -0.5), 1) for S in cand if S <= (max(lens) + 15) // 16}
-                    lib = round(time_it(args, 0, D ** -0.5), 1)   # the library's own plan
-                    best = min(res, key=res.get)
-                    by = 4 * sum(lens) * Hkv * D
-                    print(json.dumps({"shape": {"Hq": Hq, "Hkv": Hkv, "D": D}, "B": B, "ctx": ctx,
-                                      "lengths": "uniform [ctx/8, ctx]" if var else "fixed", "policy": pol,
-                                      "us_policy": res.get(pol), "us_library": lib,
-                                      "fastest": best, "us_fastest": res[best],
-                                      "GB/s_fastest": round(by / res[best] / 1e3, 1), "us_by_splits": res}),
-                          flush=True)
-                    del args
-                    torch.cuda.empty_cache()
+                lens = [ctx] * B if not var else [int(x) for x in torch.randint(ctx // 8, ctx + 1, (B,),
+                                                                                    generator=rng)]
+                args = make(lens, Hq, Hkv, D)
+                pol = mi.decode_pick_splits(B, Hkv, max(lens))
+                cand = sorted({1, 2, 4, 8, 16, 32, 64, 128, 256, pol})
+                res = {S: round(time_it(args, S, D ** -0.5), 1) for S in cand if S <= (max(lens) + 15) // 16}
+                lib = round(time_it(args, 0, D ** -0.5), 1)   # the library's own plan
+                best = min(res, key=res.get)
+                by = 4 * sum(lens) * Hkv * D
+                print(json.dumps({"shape": {"Hq": Hq, "Hkv": Hkv, "D": D}, "B": B, "ctx": ctx,
+                                  "table_tokens": B * ((max(lens) + 15) // 16) * 16,
+                                  "lengths": "uniform [ctx/8, ctx]" if var else "fixed", "policy": pol,
+                                  "us_policy": res.get(pol), "us_library": lib,
+                                  "fastest": best, "us_fastest": res[best],
+                                  "GB/s_fastest": round(by / res[best] / 1e3, 1), "us_by_splits": res}),
+                      flush=True)
+                del args
+                torch.cuda.empty_cache()
 
 
 def numerics_timing(torch, mi, dev, bf16, i32, steps: int, warmup: int):

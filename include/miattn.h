@@ -164,7 +164,7 @@ int miattn_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cach
  *            counts above max_pages_per_seq are lowered to it), or 0 for the
  *            library's plan: where miattn_decode_pick_splits would split at all,
  *            the batch holds more than one sequence and batch *
- *            max_pages_per_seq * page_size >= 2^18, every group holds the
+ *            max_pages_per_seq * page_size >= 2^17, every group holds the
  *            same number C of consecutive pages of one sequence (its last group
  *            fewer), C being the smallest size for which the batch needs at
  *            most 256 / (kv-head groups of a workgroup) groups, so sequences of

@@ -226,14 +226,14 @@ def test_repeatable_with_other_shapes_in_between():
 
 def test_policy_groups_follow_lengths():
     # num_splits = 0 on a batch the split-count policy splits and large enough
-    # for the length-proportional plan (batch x table width >= 2^18 tokens):
+    # for the length-proportional plan (batch x table width >= 2^17 tokens):
     # an empty sequence, a one-token one; parity, repeatability, and agreement
     # with fixed contiguous splits
     lens = [8192, 512, 0, 1, 6000, 700, 8191, 16, 4096, 1500] * 4
     case = synth.make_decode(3, 14, lens, 32, 8, 128, 1 / math.sqrt(128), shuffle=True, tail="nan",
                              name="policy_groups")
     assert mi.decode_pick_splits(case.batch, 8, case.max_pages * 16) > 1
-    assert case.batch * case.max_pages * 16 >= 1 << 18
+    assert case.batch * case.max_pages * 16 >= 1 << 17
     dev = to_dev(case)
     O, L = reference(case)
     o1, l1 = run(case, 0, dev)
