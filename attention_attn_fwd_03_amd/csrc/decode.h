@@ -69,7 +69,7 @@ struct DecodeArgs {
   int num_pages;
   int num_q_heads;
   int num_kv_heads;
-  int group;                    // G = Hq / Hkv (<= 8)
+  int group;                    // G = Hq / Hkv (<= 16: the columns of the score tile)
   int heads_per_wg;             // HW: kv heads served by one workgroup (8, 4, 2 or 1)
   int num_splits;
   float c;                      // scale * log2(e)
@@ -82,7 +82,9 @@ struct DecodeArgs {
 
 constexpr int kDecodeWaves = 8;
 constexpr int kDecodeThreads = 64 * kDecodeWaves;
-constexpr int kDecodeMaxGroup = 8;
+// query heads per kv head: the 16 columns of a wave's score tile (the merge
+// area of 16 heads fits inside the page staging area at every head_dim)
+constexpr int kDecodeMaxGroup = 16;
 constexpr int kPage = 16;
 // Lazy rescaling: the running max only moves when a page's max exceeds it by
 // more than this many powers of two, so the stored probabilities stay <= 2^8.

@@ -158,7 +158,7 @@ int miattn_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cach
  *            cached for each sequence (the query sees all of them)
  *   o        [batch, Hq, D] bf16 (written); lse [batch, Hq] float32 (written;
  *            may be NULL). A sequence of length 0 gives o = 0, lse = -inf.
- *   page_size must be MIATTN_PAGE_SIZE; head_dim 64, 128 or 256; Hq/Hkv <= 8
+ *   page_size must be MIATTN_PAGE_SIZE; head_dim 64, 128 or 256; Hq/Hkv <= 16
  *            (MIATTN_ERR_UNSUPPORTED otherwise).
  *   num_splits: >= 1 to fix the split count (the contiguous groups above;
  *            counts above max_pages_per_seq are lowered to it), or 0 for the

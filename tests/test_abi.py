@@ -122,7 +122,7 @@ def test_fwd_paged_empty_is_noop():
     (dict(S=-1), mi.ERR_INVALID_ARG),
     (dict(ps=32), mi.ERR_UNSUPPORTED),
     (dict(D=80), mi.ERR_UNSUPPORTED),
-    (dict(Hq=32, Hkv=2), mi.ERR_UNSUPPORTED),
+    (dict(Hq=34, Hkv=2), mi.ERR_UNSUPPORTED),
     (dict(Hq=6, Hkv=4), mi.ERR_INVALID_ARG),
     (dict(scale=float("nan")), mi.ERR_INVALID_ARG),
     (dict(mp=0), mi.ERR_INVALID_ARG),

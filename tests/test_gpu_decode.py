@@ -142,7 +142,8 @@ def test_shuffled_equals_identity_table():
         assert bitwise_equal(oi, os_) and bitwise_equal(li, ls)
 
 
-@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 128), (8, 1, 64), (16, 2, 256), (6, 3, 128)])
+@pytest.mark.parametrize("Hq,Hkv,D", [(4, 4, 128), (8, 1, 64), (16, 2, 256), (6, 3, 128),
+                                      (16, 1, 128), (24, 2, 64), (32, 2, 256), (96, 8, 128)])   # G = 12, 16
 def test_shapes(Hq, Hkv, D):
     case = synth.make_decode(30, 0, [50, 1, 129, 400], Hq, Hkv, D, 1 / math.sqrt(D), shuffle=True)
     O, L = reference(case)
@@ -244,6 +245,21 @@ def test_policy_groups_follow_lengths():
     o4, _ = run(case, 4, dev)
     mx, mean = errors(host(o1), host(o4))
     assert mx <= 1e-2 and mean <= 1e-3
+
+
+def test_group_of_16_query_heads_with_policy_groups():
+    # G = 16 (128 query heads on 8 kv heads) on a batch large enough for the
+    # length-proportional groups, and at a fixed split count
+    lens = [3000, 17, 0, 2048, 1500, 4096, 700, 2500] * 4
+    case = synth.make_decode(3, 16, lens, 128, 8, 128, 1 / math.sqrt(128), shuffle=True, tail="nan",
+                             name="g16_policy")
+    assert case.batch * case.max_pages * 16 >= 1 << 17
+    dev = to_dev(case)
+    O, L = reference(case)
+    for S in (0, 3):
+        o, l = run(case, S, dev)
+        assert_bf16_close(host(o), O, f"G=16 S={S}")
+        assert_lse_close(host(l), L, f"G=16 S={S}")
 
 
 def test_policy_groups_of_one_sequence_are_the_contiguous_splits():
