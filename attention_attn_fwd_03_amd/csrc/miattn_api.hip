@@ -20,6 +20,7 @@
 #include "decode.h"
 #include "prefill.h"
 #include "prefill_pp.h"
+#include "prefill_pair.h"
 
 // Device scratch of the no-allocation decode entry point: one copy per GPU,
 // held until the process ends. In host code `scratch` is only a stand-in for
@@ -434,7 +435,14 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
       if (pp) launch_fwd_pp<128, 2, false>(a, (int)grid, cz, st);
       else launch_fwd_c<128, fwd_qb(128), 2, false, false>(a, (int)grid, cz, st);
       break;
-    default: launch_fwd_c<256, fwd_qb(256), 1, false, true>(a, (int)grid, cz, st); break;
+    default:
+      // head_dim 256: the head dimension split over pairs of waves (same
+      // grid and work items as the four-wave kernel)
+      if (cz)
+        hipLaunchKernelGGL((miattn::miattn_prefill_pair_kernel<true>), dim3((unsigned)grid), dim3(512), 0, st, a);
+      else
+        hipLaunchKernelGGL((miattn::miattn_prefill_pair_kernel<false>), dim3((unsigned)grid), dim3(512), 0, st, a);
+      break;
   }
   const int r = check_launch("prefill bf16");
   return r ? r : ok();

@@ -1,0 +1,302 @@
+// Dense prefill at head_dim 256 on pairs of specialised waves (gfx950, bf16
+// Q/K, fp16 V).
+//
+// At head_dim 256 a wave that owns 32 query rows and does all of their work
+// holds their output (32 x 256 fp32: 128 registers) and their Q rows as
+// operands (64), so the four-wave kernel runs one wave per SIMD and nothing
+// hides its latencies. Here two waves on one SIMD share each block of 32
+// query rows and split the loop of "Streaming process" (steps 3-8) by role:
+//  * the score wave holds the Q rows and computes S^T = K Q^T for key tile t
+//    (16 MFMAs of 32x32x16 over the head dim), which it stores in LDS;
+//  * the output wave holds O, the running max and sum: it takes tile t - 1's
+//    scores from LDS, masks them, applies the lazy rescale, forms P and
+//    accumulates O^T += V^T P^T (16 MFMAs).
+// Phase k of the loop runs the score wave on tile k and the output wave on
+// tile k - 1, with a workgroup barrier after each phase, so on every SIMD
+// one wave's exponentials overlap the other's matrix-core work. Both waves
+// fit two per SIMD (about 110 and 180 registers). The copies of K(k + 1) and
+// V(k) into LDS are issued in phase k (K and V tiles double-buffered, the
+// score exchange too). Scores, softmax rule, rounding and accumulation
+// orders are those of the four-wave kernel (prefill.h), so the results are
+// the same bits. P.V runs on fp16 operands: V is converted to fp16
+// beforehand and the probabilities are rounded to fp16.
+#pragma once
+#include <type_traits>
+
+#include "common.h"
+#include "prefill.h"
+
+namespace miattn {
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(512, 1) void miattn_prefill_pair_kernel(FwdArgs a) {
+  constexpr int D = 256;
+  constexpr int BC = 32;         // keys per tile
+  constexpr int CH = D / 8;      // 16-byte chunks per row
+  constexpr int TILE_BYTES = BC * D * 2;
+  constexpr int NI = TILE_BYTES / 1024 / 8;   // 1-KB copies per wave per tensor
+  constexpr int NKK = D / 16;    // MFMA steps over the head dim
+  constexpr int NDT = D / 32;    // 32-wide output column tiles
+  using TL = FwdTile<D, 1>;
+  static_assert(TILE_BYTES % 8192 == 0, "tile must split into 1-KB copies over 8 waves");
+  // distinct LDS objects per buffer, so a copy in flight into one does not
+  // hold up reads of another
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) f32x4 xs0[4][4][64];   // scores: [pair][quad][lane]
+  __shared__ __attribute__((aligned(16))) f32x4 xs1[4][4][64];
+  auto kbuf = [&](int i) { return (MIATTN_LDS uint8_t*)(i == 0 ? k_lds0 : k_lds1); };
+  auto vbuf = [&](int i) { return (MIATTN_LDS uint8_t*)(i == 0 ? v_lds0 : v_lds1); };
+  auto xbuf = [&](int i) { return (MIATTN_LDS f32x4*)(i == 0 ? &xs0[0][0][0] : &xs1[0][0][0]); };
+
+  const int NH = a.heads_per_wg;
+  const int WQ = 4 / NH;
+  const int QR = 32 * WQ;   // query rows per tile
+
+  // --- work item: (head slot, tile pair, sequence); head slot fastest ------
+  const int lin = blockIdx.x;
+  const int hslot = lin % a.n_head_slots;
+  const int rest = lin / a.n_head_slots;
+  const int pair = rest % a.n_pairs;
+  const int b = rest / a.n_pairs;
+  int s0 = a.cu_seqlens[b];
+  int s1 = a.cu_seqlens[b + 1];
+  s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
+  s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
+  const int L = s1 - s0;
+  const int n_tiles = (L + QR - 1) / QR;
+  // query tiles i and n-1-i together cost the same for every pair (causal)
+  if (pair > n_tiles - 1 - pair) return;   // uniform over the workgroup
+  const int n_mine = pair != n_tiles - 1 - pair ? 2 : 1;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int w4 = wave & 3;               // the row block: waves w4 and w4 + 4 share a SIMD
+  const bool score_wave = wave < 4;
+  const int hs = w4 % NH;
+  const int qs = w4 / NH;
+  const int gpw = a.group / NH;
+  const int g = hslot / gpw;
+  const int h = g * a.group + (hslot % gpw) * NH + hs;
+  const int half = lane >> 5;
+  const int Hq = a.num_q_heads;
+  const int Hkv = a.num_kv_heads;
+  const float c = a.c;
+
+  const size_t kv_row = (size_t)Hkv * D;
+  const uint16_t* kbase = a.k + (size_t)s0 * kv_row + (size_t)g * D;
+  const uint16_t* vbase = a.v + (size_t)s0 * kv_row + (size_t)g * D;
+
+  // Direct global -> LDS copies of a K or V tile: lane i of copy j of this
+  // wave fills slot lidx % CH of row lidx / CH (lidx = (wave NI + j) 64 + i)
+  // with the chunk the swizzle maps there; rows past the sequence end repeat
+  // its last row (their scores are masked).
+  uint32_t koff[NI], voff[NI];
+#pragma unroll
+  for (int j = 0; j < NI; ++j) {
+    const int lidx = (wave * NI + j) * 64 + lane;
+    const int r = lidx / CH;
+    const int slot = lidx % CH;
+    koff[j] = (uint32_t)(((size_t)r * kv_row + 8 * (slot ^ TL::kswz(r))) * 2);
+    voff[j] = (uint32_t)(((size_t)r * kv_row + 8 * (slot ^ TL::vswz(r))) * 2);
+  }
+  const uint64_t tile_bytes = (uint64_t)BC * kv_row * 2;
+  auto back_off = [&](int kt, int j) -> uint32_t {   // tail tile: rows past the end repeat the last one
+    const int r = ((wave * NI + j) * 64 + lane) / CH;
+    const int rr = kt * BC + r < L ? r : L - 1 - kt * BC;
+    return (uint32_t)((size_t)(r - rr) * kv_row * 2);
+  };
+  auto load_k = [&](int kt, int buf) {
+    const bool full = (kt + 1) * BC <= L;
+    const char* b0 = (const char*)kbase + (uint64_t)kt * tile_bytes;
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      dma16_to_lds(b0, koff[j] - (full ? 0u : back_off(kt, j)), kbuf(buf) + (wave * NI + j) * 1024);
+  };
+  auto load_v = [&](int kt, int buf) {
+    const bool full = (kt + 1) * BC <= L;
+    const char* b0 = (const char*)vbase + (uint64_t)kt * tile_bytes;
+#pragma unroll
+    for (int j = 0; j < NI; ++j)
+      dma16_to_lds(b0, voff[j] - (full ? 0u : back_off(kt, j)), vbuf(buf) + (wave * NI + j) * 1024);
+  };
+
+  const int bb = lane >> 4, kq = lane & 15;
+  const int r_k = lane & 31;   // K row this lane reads as the A operand
+
+  for (int tsel = 0; tsel < n_mine; ++tsel) {
+    const int qt = tsel == 0 ? pair : n_tiles - 1 - pair;
+    const int q0 = qt * QR + 32 * qs;   // first query row of this block
+    const int qt_end = qt * QR + QR;
+    const int kend_wg = CAUSAL ? (qt_end < L ? qt_end : L) : L;
+    const int n_kt = (kend_wg + BC - 1) / BC;
+    const int kend_w = CAUSAL ? (q0 + 32 < L ? q0 + 32 : L) : L;
+    const int n_kt_w = q0 < L ? (kend_w + BC - 1) / BC : 0;   // tiles this block computes
+
+    // The two roles run separate loops (so neither keeps the other's
+    // registers live) with the same barriers: one or two before phase 0,
+    // one after each of the n_kt + 1 phases. Phase k: the score wave on tile
+    // k (K buffer k & 1, scores into exchange buffer k & 1), the output wave
+    // on tile k - 1; every wave issues its share of the copies of K(k + 1)
+    // and V(k).
+    if (score_wave) {
+      // Q rows as B operands: row q0 + lane%32, columns 16 kk + 8 half .. + 7
+      u32x4 qop[NKK];
+      {
+        const int row = q0 + (lane & 31);
+        const bool ok = row < L;
+        const uint16_t* qp = a.q + ((size_t)(s0 + (ok ? row : 0)) * Hq + h) * D + 8 * half;
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const u32x4 z = {0u, 0u, 0u, 0u};
+          qop[kk] = ok ? ld16(qp + 16 * kk) : z;
+        }
+      }
+      if (tsel > 0) __syncthreads();   // previous tile's last reads before the buffers are refilled
+      if (n_kt > 0) load_k(0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      auto phase = [&](int k, auto parc) {
+        constexpr int par = decltype(parc)::value;   // k & 1
+        if (k + 1 < n_kt) load_k(k + 1, par ^ 1);
+        if (k < n_kt) load_v(k, par);
+        if (k < n_kt_w) {
+          f32x16 s;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[r] = 0.f;
+          const MIATTN_LDS uint8_t* kr = kbuf(par) + r_k * (2 * D);
+#pragma unroll
+          for (int kk = 0; kk < NKK; ++kk) {
+            const bf16x8 kop = as_bf16x8(lds_ld16(kr + 16 * ((2 * kk + half) ^ TL::kswz(r_k))));
+            s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kop, as_bf16x8(qop[kk]), s, 0, 0, 0);
+          }
+          MIATTN_LDS f32x4* xo = xbuf(par) + w4 * 256;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            xo[r4 * 64 + lane] = (f32x4){s[4 * r4], s[4 * r4 + 1], s[4 * r4 + 2], s[4 * r4 + 3]};
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      };
+      for (int k = 0; k <= n_kt; k += 2) {
+        phase(k, std::integral_constant<int, 0>{});
+        if (k + 1 <= n_kt) phase(k + 1, std::integral_constant<int, 1>{});
+      }
+    } else {
+      float m = kNegInf, l = 0.f;
+      f32x16 acc[NDT];
+#pragma unroll
+      for (int i = 0; i < NDT; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+      if (tsel > 0) __syncthreads();
+      if (n_kt > 0) load_k(0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      auto phase = [&](int k, auto parc) {
+        constexpr int par = decltype(parc)::value;   // k & 1
+        if (k + 1 < n_kt) load_k(k + 1, par ^ 1);
+        if (k < n_kt) load_v(k, par);
+        const int kt = k - 1;
+        if (kt >= 0 && kt < n_kt_w) {
+          const MIATTN_LDS f32x4* xi = xbuf(par ^ 1) + w4 * 256;
+          f32x16 s;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 o = xi[r4 * 64 + lane];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[4 * r4 + e] = o[e];
+          }
+          // mask (diagonal / tail tiles only): key of score r is kt BC +
+          // 4 half + 8 (r / 4) + r % 4, kept iff that offset is below lim
+          const bool need_mask = (kt + 1) * BC > L || (CAUSAL && (kt + 1) * BC - 1 > q0);
+          if (need_mask) {
+            const int kbase_lane = kt * BC + 4 * half;
+            int lim = L - kbase_lane;
+            if (CAUSAL) {
+              const int lc = q0 + (lane & 31) + 1 - kbase_lane;
+              lim = lc < lim ? lc : lim;
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[r] = (8 * (r >> 2) + (r & 3)) < lim ? s[r] : kNegInf;
+          }
+          // tile max and lazy rescale (the running max moves only when the
+          // tile's max exceeds it by more than 2^8)
+          float smax = kNegInf;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) smax = fmaxf(smax, s[r]);
+          smax = fmaxf(smax, xor32(smax));
+          const float tmax = smax * c;   // scale > 0, so max(s c) = c max(s)
+          if (__builtin_amdgcn_ballot_w64(tmax > m + kFwdRescaleThreshold)) {
+            const float mn = fmaxf(m, tmax);
+            const float alpha = (m == kNegInf) ? 0.f : exp2_hw(m - mn);
+            l *= alpha;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) acc[dt] *= alpha;
+            m = mn;
+          }
+          // P = exp2(s c - m), rounded to fp16 for P.V; the tile's row sum
+          // adds the fp32 values in score order, then l += ls
+          const float nmu = (m == kNegInf) ? 0.f : -m;
+          float ls = 0.f;
+          u32x4 pw[2];
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = exp2_hw(__builtin_fmaf(s[r], c, nmu));
+            const float p1 = exp2_hw(__builtin_fmaf(s[r + 1], c, nmu));
+            ls += p0 + p1;
+            pw[r >> 3][(r >> 1) & 3] = pack_f16x2(p0, p1);
+          }
+          // O^T += V^T P^T; V^T rows via the transposing read: block bb of
+          // 16 lanes reads keys 16u + 4(bb/2) + {0..3} (+8), columns 32 dt +
+          // 16 (bb%2) + {0..15}
+          const MIATTN_LDS uint8_t* vl = vbuf(par ^ 1);
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int r0 = 16 * u + 4 * (bb >> 1) + (kq >> 2);
+            const int r1 = r0 + 8;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+              const int col = 32 * dt + 16 * (bb & 1) + 4 * (kq & 3);
+              const int ch = col >> 3, sub = (col & 7) * 2;
+              const u32x2 lo = lds_ld_tr16(vl + r0 * (2 * D) + 16 * (ch ^ TL::vswz(r0)) + sub);
+              const u32x2 hi = lds_ld_tr16(vl + r1 * (2 * D) + 16 * (ch ^ TL::vswz(r1)) + sub);
+              acc[dt] = mfma_pv<true>(lo, hi, pw[u], acc[dt]);
+            }
+          }
+          l += ls;
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      };
+      for (int k = 0; k <= n_kt; k += 2) {
+        phase(k, std::integral_constant<int, 0>{});
+        if (k + 1 <= n_kt) phase(k + 1, std::integral_constant<int, 1>{});
+      }
+
+      // --- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 -------------------
+      const float lt = l + xor32(l);
+      const int qrow = q0 + (lane & 31);
+      if (qrow < L) {
+        const bool empty = !(lt > 0.f);
+        const float inv = empty ? 0.f : 1.f / lt;
+        uint16_t* op = a.o + ((size_t)(s0 + qrow) * Hq + h) * D + 4 * half;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x16& A = acc[dt];
+            u32x2 w = {pack_bf16x2(A[4 * r4] * inv, A[4 * r4 + 1] * inv),
+                       pack_bf16x2(A[4 * r4 + 2] * inv, A[4 * r4 + 3] * inv)};
+            *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * r4) = w;
+          }
+        if (a.lse != nullptr && half == 0)
+          a.lse[(size_t)h * a.total_tokens + s0 + qrow] = empty ? kNegInf : (m + log2_hw(lt)) * kLn2;
+      }
+    }
+  }
+}
+
+}  // namespace miattn
