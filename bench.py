@@ -482,6 +482,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode-splits", type=int, default=0, help="0 = library policy")
     ap.add_argument("--long-splits", type=int, default=0, help="0 = library policy")
+    ap.add_argument("--long-ctx", type=int, default=131072,
+                    help="context of the long decode (only with --only long: the step keeps 131072)")
+    ap.add_argument("--flush-each", action="store_true",
+                    help="with --only: read a 512 MB scratch buffer before every call, so inputs below the "
+                         "last-level cache come from HBM (the printed mean then includes the reads; per-kernel "
+                         "times come from a kernel trace)")
     ap.add_argument("--only", choices=["prefill", "decode", "long", "chunked", "backward", "varlen", "copy"],
                     default=None,
                     help="profiling aid: run just one stage (or a 1 GiB device copy used to calibrate "
@@ -507,6 +513,10 @@ def main():
         print(json.dumps({"error": "this build runs on one GPU only; multi-GPU sharding is a design note, "
                                    "not implemented", "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
+    if args.long_ctx != 131072 and args.only != "long":
+        ap.error("--long-ctx changes the long decode's context; use it with --only long")
+    if args.flush_each and args.only is None:
+        ap.error("--flush-each applies to --only runs")
 
     import torch
     import attention_attn_fwd_03_amd as mi
@@ -579,7 +589,7 @@ def main():
         Dd["lse"] = torch.empty((dc.batch, dc.num_q_heads), dtype=torch.float32, device=dev)
         # 0 = the library's policy (length-proportional groups where it splits)
         dsplits = args.decode_splits
-    lc = synth.config4(ctx=131072, seed=0) if "long" in want else None
+    lc = synth.config4(ctx=args.long_ctx, seed=0) if "long" in want else None
     if lc is not None:
         Ld = dict(q=bf16(lc.q), kc=bf16(lc.k_cache), vc=bf16(lc.v_cache), bt=i32(lc.block_table),
                   sl=i32(lc.seq_lens))
@@ -640,6 +650,13 @@ def main():
     if args.only is not None:
         f = {"prefill": prefill, "decode": decode, "long": long_decode, "chunked": chunked,
              "backward": backward, "varlen": varlen}[args.only]
+        if args.flush_each:
+            flush = torch.ones(512 << 20, dtype=torch.uint8, device=dev)
+            f_run = f
+
+            def f():
+                flush.max()   # read-only: leaves no dirty lines behind
+                f_run()
         settle([f])
         for _ in range(args.warmup):
             f()
