@@ -109,8 +109,9 @@ void launch_fwd_c(const miattn::FwdArgs& a, int grid, bool causal, hipStream_t s
   else launch_fwd<D, QB, KB, false, PAGED, F16V>(a, grid, st);
 }
 
-// query blocks of 32 rows per wave for each head_dim
-constexpr int fwd_qb(int d) { return d >= 256 ? 1 : 1; }
+// query blocks of 32 rows per wave in the four-wave kernel: one at every
+// head_dim (the template keeps QB as a parameter)
+constexpr int fwd_qb(int) { return 1; }
 
 // Dense prefill with head_dim 64 and 128 runs the eight-wave ping-pong kernel
 // (two 32-row groups per query tile) when its grid has at least one

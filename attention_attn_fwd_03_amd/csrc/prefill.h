@@ -9,10 +9,9 @@
 // MI355X mapping:
 //  * Workgroup = 4 waves, one per SIMD. Waves split the NH query heads of one
 //    kv-head group (NH: the largest of 4, 2, 1 dividing G) and 4/NH row ranges; each wave owns QB
-//    blocks of 32 query rows (64 rows for head_dim <= 128), so every K and V
-//    operand read from LDS feeds QB MFMAs (LDS bytes per flop halve at QB=2)
-//    and all waves reuse the same K/V tile (GQA sharing of "GPU Datapath",
-//    section C).
+//    blocks of 32 query rows (the library launches QB = 1), so every K and V
+//    operand read from LDS feeds QB MFMAs, and all waves reuse the same K/V
+//    tile (GQA sharing of "GPU Datapath", section C).
 //  * K/V tiles of Bc = 32*KB keys are double-buffered in LDS and copied
 //    straight from HBM into LDS (buffer loads in their LDS form, 16 bytes per
 //    lane, whole rows per 16 lanes) one tile ahead, into a swizzled layout
