@@ -497,13 +497,24 @@ __global__ __launch_bounds__(512) void miattn_prefill_fwd_f32_kernel(FwdF32Args 
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads;
   const size_t kv_row = (size_t)Hkv * D;
 
-  // Q operand: lane holds d = 2 st + half for st = 0..31
+  // Q operand: at product step st, lane half `half` supplies d = 32 half +
+  // st, so a lane's 32 values are one contiguous 128-byte piece of its row
+  // (eight 16-byte loads; one float per lane from scattered rows made every
+  // load instruction touch 32-64 cache lines, and the address unit, shared
+  // by the workgroup's waves, was the bottleneck). Every operand load reads a
+  // valid (clamped) address unconditionally and the value is zeroed
+  // afterwards: a load under a condition becomes a branch around it, and the
+  // compiler then waits for each load right before its product.
   float qv[32];
   {
     const bool ok = qrow < L;
-    const float* qp = a.q + ((size_t)(s0 + (ok ? qrow : 0)) * Hq + h) * D + half;
+    const float* qp = a.q + ((size_t)(s0 + (ok ? qrow : 0)) * Hq + h) * D + 32 * half;
 #pragma unroll
-    for (int st = 0; st < 32; ++st) qv[st] = ok ? qp[2 * st] : 0.f;
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(qp + 4 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qv[4 * i + e] = ok ? t[e] : 0.f;
+    }
   }
   const int kend = CAUSAL ? (L < q0 + 32 ? L : q0 + 32) : L;
   float m = kNegInf, l = 0.f;
@@ -523,18 +534,28 @@ __global__ __launch_bounds__(512) void miattn_prefill_fwd_f32_kernel(FwdF32Args 
       const bool ok = key < L;
       const float* vp = vb + (size_t)(ok ? key : 0) * kv_row + (lane & 31);
 #pragma unroll
-      for (int dt = 0; dt < 2; ++dt) vv[r][dt] = ok ? vp[32 * dt] : 0.f;
+      for (int dt = 0; dt < 2; ++dt) vv[r][dt] = vp[32 * dt];
+#pragma unroll
+      for (int dt = 0; dt < 2; ++dt) vv[r][dt] = ok ? vv[r][dt] : 0.f;
     }
-    // S^T (32 keys x 32 queries); A = K (row key k0 + lane%32, col d = 2 st + half)
+    // S^T (32 keys x 32 queries); A = K (row key k0 + lane%32, col d = 32 half + st)
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
     const int krow = k0 + (lane & 31);
     const bool kok = krow < L;
-    const float* kp = kb + (size_t)(kok ? krow : 0) * kv_row + half;
+    const float* kp = kb + (size_t)(kok ? krow : 0) * kv_row + 32 * half;
+    float kv[32];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const f32x4 t = *reinterpret_cast<const f32x4*>(kp + 4 * i);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kv[4 * i + e] = t[e];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // all of the tile's loads issued before the products
 #pragma unroll
     for (int st = 0; st < 32; ++st)
-      s = __builtin_amdgcn_mfma_f32_32x32x2f32(kok ? kp[2 * st] : 0.f, qv[st], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x2f32(kok ? kv[st] : 0.f, qv[st], s, 0, 0, 0);
     float tmax = kNegInf;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {

@@ -133,6 +133,16 @@ def test_zero_length_sequences_and_single_tokens():
     full_check(synth.make_prefill(21, 0, [0, 1, 0, 5, 1], 8, 2, 128, 0.1, True, "bf16", "degenerate"))
 
 
+@pytest.mark.parametrize("Hq,Hkv,causal", [(16, 4, True), (4, 4, False), (4, 2, True), (6, 2, False)])
+def test_head_dim_256_pairs_degenerate_and_ragged(Hq, Hkv, causal):
+    # the head_dim-256 pair kernel on empty sequences, single tokens, a
+    # sequence ending one row into a tile and one a row short of two tiles,
+    # for group sizes 4, 1, 2 and 3 (four, one, two and one query heads per
+    # workgroup)
+    full_check(synth.make_prefill(21, Hq + Hkv, [0, 1, 33, 0, 63, 2, 97], Hq, Hkv, 256, 2.0 ** -4, causal, "bf16",
+                                  f"d256_degenerate_{Hq}x{Hkv}"))
+
+
 def test_bitwise_repeatable():
     case = synth.config2(S=1024, seed=1)
     o1, l1 = run(case)
