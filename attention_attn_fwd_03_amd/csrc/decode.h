@@ -374,6 +374,36 @@ __global__ __launch_bounds__(kDecodeThreads, 1) void miattn_decode_split_kernel(
   l += xor16(l);
   l += xor32(l);
 
+  if (!STUDY && WPH == 1) {
+    // One wave per kv head: the wave holds its heads' whole result, so it
+    // normalises and stores it from registers, with no barrier and no LDS
+    // round trip (the merge below would weigh it by exp2(0) = 1: the same
+    // bits). Lane: query head hl of kv head g, columns 16 dt + 4 quad .. + 3.
+    if (hl < G) {
+      const bool empty = !(l > 0.f);
+      const float inv = empty ? 0.f : 1.f / l;
+      const float lse = empty ? kNegInf : (m + log2_hw(l)) * kLn2;
+      const size_t row = (size_t)b * a.num_q_heads + (size_t)g * G + hl;
+      if (!balanced && S == 1) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const f32x4 o = acc[dt] * inv;
+          u32x2 w2 = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          *reinterpret_cast<u32x2*>(a.o + row * D + 16 * dt + 4 * quad) = w2;
+        }
+        if (a.lse != nullptr && quad == 0) a.lse[row] = lse;
+      } else {
+        const size_t slot = balanced ? (size_t)(split * a.num_q_heads) + (row - (size_t)b * a.num_q_heads)
+                                     : row * S + split;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+          *reinterpret_cast<f32x4*>(a.part_o + slot * D + 16 * dt + 4 * quad) = acc[dt] * inv;
+        if (quad == 0) a.part_lse[slot] = lse;
+      }
+    }
+    return;
+  }
+
   __syncthreads();   // staging area is reused for the merge below
   float* mo = (float*)smem;                                                // [wave][G][D]
   float* mm = (float*)(smem + (Smem::kBytes - 2 * kDecodeWaves * 16 * 4)); // [wave][16]
