@@ -11,16 +11,18 @@
 // splits into two phases:
 //   GEMM(t): O += P(t-1) V(t-1) and S(t) = K(t) Q^T   (32 MFMAs for D = 128)
 //   SOFT(t): mask, exponentials, P(t) in bf16          (vector ALU only)
-// and the loop runs phase by phase with a workgroup barrier between phases.
-// Group 1 runs one phase behind group 0, so in every phase one wave of each
-// SIMD issues MFMAs while the other computes exponentials.
+// Group 1 runs one phase behind group 0: with one workgroup barrier per
+// tile, interval t holds GEMM(t), SOFT(t) for group 0 and SOFT(t - 1),
+// GEMM(t) for group 1, so one wave of each SIMD issues MFMAs while the other
+// computes exponentials, first one way round, then the other. Both groups
+// walk the same program order; only their barriers sit at different points.
 //
-// K(t) is read in phases 2t (group 0) and 2t + 1 (group 1), V(t) in phases
-// 2t + 2 and 2t + 3. In phase 2u the workgroup starts the direct HBM->LDS
-// copies of K(u + 1) and V(u) into the buffers that K(u - 1) and V(u - 2)
-// held (their last readers finished in phase 2u - 1); every wave waits for
-// its share at the end of phase 2u + 1, before the barrier, so both tiles are
-// in LDS when phase 2u + 2 reads them. Two buffers each for K and V. A
+// Every wave of interval t reads K(t) and V(t - 1). At the start of interval
+// u each wave starts its share of the direct HBM->LDS copies of K(u + 1) and
+// V(u) into the buffers that K(u - 1) and V(u - 2) held (read last in
+// interval u - 1, closed by the barrier) and waits for them at the end of
+// interval u, before the barrier, so both tiles are in LDS when interval
+// u + 1 reads them. Two buffers each for K and V. A
 // workgroup takes two query tiles in turn; the second tile's Q rows are
 // loaded in the first one's last step (its last S is done, no copy is in
 // flight), so their latency hides behind the last P V and the epilogue.
@@ -316,34 +318,37 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
       l += ls;
     };
 
-    // Global phases 0 .. 2 n_kt + 1, a barrier after each. Group 0 runs
-    // GEMM(i) in phase 2i and SOFT(i) in phase 2i + 1; group 1 idles in
-    // phase 0 and runs GEMM(i) in 2i + 1, SOFT(i) in 2i + 2. Both walk the
-    // same sequence GEMM(i), SOFT(i) in program order, so the accumulators
-    // keep one register home. Copies for u start in phase 2u and are waited
-    // for at the end of phase 2u + 1, by every wave for its own share.
+    // Both groups walk the same sequence GEMM(i), SOFT(i) in program order,
+    // so the accumulators keep one register home (two orders, one per group,
+    // made the compiler copy them between homes and spill).
     auto copies = [&](int u) __attribute__((always_inline)) {
       if (u + 1 < n_kt) copy_tile(u + 1, kbase, koff, lds_addr(kbuf((u + 1) & 1)));
       if (u < n_kt) copy_tile(u, vbase, voff, lds_addr(vbuf(u & 1)));
     };
-    if (grp == 1) {
-      copies(0);
-      __syncthreads();
-    }
-    // In the last step (i = n_kt) no copy is in flight and Q is dead (the
-    // last S was in step n_kt - 1): the next query tile's Q rows are loaded
-    // there and travel through the last P V and the epilogue; the next
-    // pass's first wait covers them.
+    // One barrier per tile: interval i is GEMM(i), SOFT(i) for group 0 and
+    // SOFT(i - 1), GEMM(i) for group 1 (the same program order, the barriers
+    // at different points); every wave of interval i reads K(i) and V(i - 1),
+    // and each wave issues its share of the copies of K(i + 1) and V(i) right
+    // after the barrier that opens the interval and waits for it at its end.
+    // In the last interval (i = n_kt) no copy is in flight and Q is dead (the
+    // last S was in interval n_kt - 1): the next query tile's Q rows are
+    // loaded there and travel through the last P V and the epilogue; the
+    // next pass's first wait covers them.
+    if (grp == 1) copies(0);
     for (int i = 0; i <= n_kt; ++i) {
       if (i == n_kt && tsel + 1 < n_mine) load_q(tile_of(tsel + 1));
-      gemm(i);
       if (grp == 0) copies(i);
-      if (grp == 1 && i < n_kt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
+      gemm(i);
+      if (grp == 1) {
+        if (i < n_kt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        copies(i + 1);
+      }
       if (i < n_kt) soft(i);
-      if (grp == 1 && i + 1 <= n_kt) copies(i + 1);
-      if (grp == 0 && i < n_kt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      if (grp == 0 || i < n_kt) __syncthreads();
+      if (grp == 0) {
+        if (i < n_kt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+      }
     }
 
     // --- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 --------------------
