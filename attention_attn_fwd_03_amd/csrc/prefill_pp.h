@@ -338,7 +338,11 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
     for (int i = 0; i <= n_kt; ++i) {
       if (i == n_kt && tsel + 1 < n_mine) load_q(tile_of(tsel + 1));
       if (grp == 0) copies(i);
+      // the wave in its MFMA half of the interval issues first when both
+      // waves of a SIMD have an instruction ready
+      __builtin_amdgcn_s_setprio(1);
       gemm(i);
+      __builtin_amdgcn_s_setprio(0);
       if (grp == 1) {
         if (i < n_kt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
