@@ -12,18 +12,17 @@
 //  * prep: Delta = rowsum(dO * O) in fp32, the LSE in log2 units (both in
 //    rows padded by 32 so tile-sized copies stay in bounds), and fp16 copies
 //    of Q, dO, K and V, in one pass over the inputs.
-//  * dK/dV: one workgroup of 4 waves per (kv head, 32 keys, sequence). The
-//    32 keys' K and V sit in LDS (copied once, read back as MFMA operands at
-//    every step); every wave holds dK^T, dV^T accumulators in registers and
-//    takes every fourth (query head, 32-query tile) step of the group, with
-//    its own double-buffered Q/dO tiles copied straight from HBM into LDS; the
-//    waves never wait for each other until the end, where their four partial
-//    sums are added through LDS in a fixed order. Per tile: S = Q K^T and dP = dO V^T (query rows, key columns),
-//    then dV^T += dO^T P and dK^T += Q^T dS: the accumulator registers of P
-//    and dS, rounded to fp16, are the B operand as they stand; dO^T and Q^T
-//    come from the same LDS tile through the transposing read. At head_dim
-//    256 the four waves share each Q/dO tile and split 64 keys instead
-//    (miattn_bwd_dkdv_d256_kernel).
+//  * dK/dV: one workgroup of 8 waves per (kv head, 64 keys, sequence), two
+//    per SIMD: the two waves of a SIMD take 32 keys each and share a
+//    double-buffered Q/dO tile pair copied straight from HBM into LDS, and
+//    the four pairs take every fourth (query head, 32-query tile) step of the
+//    group; the four partial sums of each key are added through LDS in a
+//    fixed order at the end. Per tile: S = Q K^T and dP = dO V^T (query rows,
+//    key columns), then dV^T += dO^T P and dK^T += Q^T dS: the accumulator
+//    registers of P and dS, rounded to fp16, are the B operand as they
+//    stand; dO^T and Q^T come from the same LDS tile through the transposing
+//    read. At head_dim 256 four waves share each Q/dO tile and split 64 keys,
+//    16 each (miattn_bwd_dkdv_d256_kernel).
 //  * dQ: the forward's orientation: one wave per 32 query rows of one head,
 //    S^T = K Q^T and dP^T = V dO^T with Q, dO held as operands, K/V tiles
 //    streaming through LDS, dQ^T += K^T dS^T with K^T read transposed.
@@ -136,32 +135,49 @@ __global__ __launch_bounds__(256) void miattn_bwd_prep_kernel(BwdArgs a) {
   }
 }
 
-// ---------------------------------------------------------------- dK / dV
+// ---------------------------------------------------------------- dK / dV, head_dim 64 and 128
+// Two waves per SIMD. (With four waves that each own a double-buffered Q/dO
+// tile pair, the LDS, 146 KB, and the registers, 328, allow one.) A
+// workgroup of eight waves covers 64 keys; waves p and p + 4 run on the same
+// SIMD, take keys 0-31 and 32-63 of the block, and walk the same steps p,
+// p + 4, ... of the group's (query head, 32-query tile) list, so they share one
+// double-buffered Q/dO tile pair, each copying half of it. Every wave holds
+// the dV^T, dK^T accumulators of its 32 keys and their V operands in
+// registers and reads the K operands from LDS (the 64 keys' K sit there for
+// the whole loop), which brings it to two waves per SIMD. The pairs keep
+// step with one workgroup barrier per step; a step whose queries all precede
+// a wave's keys (causal) is skipped by that wave. The four partial sums of
+// each 32-key half are added in pair order, one half after the other, through
+// the Q/dO buffers.
+// Per step: S = Q K^T and dP = dO V^T (query rows, key columns), then
+// dV^T += dO^T P and dK^T += Q^T dS with P and dS, rounded to fp16, taken
+// from the accumulators as B operands as they stand and dO^T, Q^T read from
+// the same LDS tile through the transposing read. The tile swizzle serves
+// both read shapes (BwdTile).
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(512, 1) void miattn_bwd_dkdv_pair_kernel(BwdArgs a) {
   using TL = BwdTile<D>;
   constexpr int CH = TL::CH;
   constexpr int NKK = D / 16;                        // MFMA steps over the head dim
   constexpr int NDT = D / 32;                        // 32-wide d blocks of dK^T / dV^T
   constexpr int QT = 32;                             // queries per tile
-  constexpr int TILE = QT * D * 2;                   // bytes of one Q or dO tile
-  constexpr int NC = TILE / 1024;                    // 1-KB copies per tensor and tile
-  static_assert(TILE % 1024 == 0, "tile must split into 1-KB copies");
-  static_assert(2 * QT * D * 4 <= 4 * TILE, "two waves' fp32 partials must fit one tile array");
-  // wave w owns bytes [w TILE, (w+1) TILE) of each array; four separate LDS
-  // objects so that a copy in flight into one buffer does not hold up reads
-  // of the other
+  constexpr int TILE = QT * D * 2;                   // bytes of one 32-row tile
+  constexpr int NC = TILE / 1024;                    // 1-KB copies per tile
+  constexpr int NCH = NC / 2;                        // ... issued by each wave of a pair
+  static_assert(NC % 2 == 0, "a tile must split into 1-KB copies over two waves");
+  static_assert(2 * QT * D * 4 <= 4 * TILE, "two pairs' fp32 partials must fit one tile array");
+  // [pair] tiles; four distinct LDS objects, so that a copy in flight into
+  // one buffer does not hold up reads of the other
   __shared__ __attribute__((aligned(1024))) uint8_t q_lds0[4 * TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t q_lds1[4 * TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t d_lds0[4 * TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t d_lds1[4 * TILE];
-  __shared__ __attribute__((aligned(16))) float st_lds0[4 * 64];   // per wave: 32 LSE, 32 Delta
+  __shared__ __attribute__((aligned(16))) float st_lds0[4 * 64];   // per pair: 32 LSE, 32 Delta
   __shared__ __attribute__((aligned(16))) float st_lds1[4 * 64];
-  __shared__ __attribute__((aligned(1024))) uint8_t kv_lds[2 * TILE];   // the 32 keys' K, then V
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds[2 * TILE];   // K of the 64 keys
 
-  // work item: (kv head, key block, sequence), kv head fastest, sequence
-  // slowest (the workgroups resident together read one sequence's Q/dO, which
-  // then stays in L2); key block 0 (the most causal work) first
+  // work item: (kv head, 64-key block, sequence), kv head fastest, sequence
+  // slowest; key block 0 (the most causal work) first
   const int lin = blockIdx.x;
   const int g = lin % a.num_kv_heads;
   const int rest = lin / a.num_kv_heads;
@@ -172,82 +188,83 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
   s0 = s0 < 0 ? 0 : (s0 > a.total_tokens ? a.total_tokens : s0);
   s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
   const int L = s1 - s0;
-  const int kb0 = kblk * 32;
+  const int kb0 = kblk * 64;
   if (kb0 >= L) return;   // uniform over the workgroup
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pr = wave & 3;         // the pair (and SIMD)
+  const int kh = wave >> 2;        // the pair's key half
   const int half = lane >> 5;
   const int bb = lane >> 4, kq = lane & 15;
   const int Hq = a.num_q_heads, Hkv = a.num_kv_heads, G = a.group;
   const float c = a.c;
-  const int key = kb0 + (lane & 31);                 // this lane's key column
+  const int kw0 = kb0 + 32 * kh;                     // this wave's first key
+  const int key = kw0 + (lane & 31);                 // this lane's key column
   const bool key_ok = key < L;
 
-  // this wave's buffers: LDS byte addresses (the copies are issued from asm)
-  const uint32_t qaddr0 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)q_lds0 + wave * TILE);
-  const uint32_t qaddr1 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)q_lds1 + wave * TILE);
-  const uint32_t daddr0 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)d_lds0 + wave * TILE);
-  const uint32_t daddr1 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)d_lds1 + wave * TILE);
-  const uint32_t saddr0 = (uint32_t)(uintptr_t)((MIATTN_LDS float*)st_lds0 + wave * 64);
-  const uint32_t saddr1 = (uint32_t)(uintptr_t)((MIATTN_LDS float*)st_lds1 + wave * 64);
+  const uint32_t qaddr0 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)q_lds0 + pr * TILE);
+  const uint32_t qaddr1 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)q_lds1 + pr * TILE);
+  const uint32_t daddr0 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)d_lds0 + pr * TILE);
+  const uint32_t daddr1 = (uint32_t)(uintptr_t)((MIATTN_LDS uint8_t*)d_lds1 + pr * TILE);
+  const uint32_t saddr0 = (uint32_t)(uintptr_t)((MIATTN_LDS float*)st_lds0 + pr * 64);
+  const uint32_t saddr1 = (uint32_t)(uintptr_t)((MIATTN_LDS float*)st_lds1 + pr * 64);
 
-  // K, V of the 32 keys (fp16 copies) in LDS, swizzled like the Q/dO tiles,
-  // read as B operands (lane: key lane%32, d = 16 kk + 8 half + 0..7) at the
-  // same offsets as the Q/dO operand reads; keys past the sequence end
-  // repeat its last key (their P and dS are masked to 0). Each wave copies
-  // NC/4 of the 1-KB pieces of each.
+  // K of the 64 keys into k_lds and their V into q_lds1 (which no step fills
+  // before the loop starts), swizzled like the Q/dO tiles; keys past the
+  // sequence end repeat its last key (their P and dS are masked to 0)
   {
     const size_t kv_row = (size_t)Hkv * D;
     const char* ksrc = (const char*)(a.k16 + (size_t)(s0 + kb0) * kv_row + (size_t)g * D);
     const char* vsrc = (const char*)(a.v16 + (size_t)(s0 + kb0) * kv_row + (size_t)g * D);
 #pragma unroll
-    for (int j = wave; j < NC; j += 4) {
+    for (int j = wave; j < 2 * NC; j += 8) {
       const int lidx = j * 64 + lane;
       const int r = lidx / CH;
       const int slot = lidx % CH;
       const int rr = kb0 + r < L ? r : L - 1 - kb0;
       const uint32_t off = (uint32_t)(((size_t)rr * kv_row + 8 * (slot ^ TL::swz(r))) * 2);
-      dma16_to_lds(ksrc, off, (MIATTN_LDS uint8_t*)kv_lds + j * 1024);
-      dma16_to_lds(vsrc, off, (MIATTN_LDS uint8_t*)kv_lds + TILE + j * 1024);
+      dma16_to_lds(ksrc, off, (MIATTN_LDS uint8_t*)k_lds + j * 1024);
+      dma16_to_lds(vsrc, off, (MIATTN_LDS uint8_t*)q_lds1 + j * 1024);
     }
   }
-  const MIATTN_LDS uint8_t* k_l = (const MIATTN_LDS uint8_t*)kv_lds;
-  const MIATTN_LDS uint8_t* v_l = (const MIATTN_LDS uint8_t*)kv_lds + TILE;
+  const MIATTN_LDS uint8_t* k_l = (const MIATTN_LDS uint8_t*)k_lds;
 
   // steps: (query head of the group, query tile); causal tiles start at the
-  // one holding query kb0; this wave takes steps wave, wave + 4, ...
+  // one holding query kb0; pair p takes steps p, p + 4, ...
   const int n_qt = (L + QT - 1) / QT;
   const int qt0 = CAUSAL ? kb0 / QT : 0;
   const int nq = n_qt - qt0;
   const int n_steps = G * nq;
-  const int n_mine = n_steps > wave ? (n_steps - wave + 3) / 4 : 0;
+  const int n_mine = n_steps > pr ? (n_steps - pr + 3) / 4 : 0;
+  const int n_iter = (n_steps + 3) / 4;             // pair 0's count, the most
 
-  // copy j of a tile: lane fills slot lidx % CH of row lidx / CH (lidx =
-  // 64 j + lane) with the chunk the swizzle maps there; rows past the
-  // sequence end repeat its last row (their P and dS are masked to 0)
+  // copy j of a tile (this wave: j = kh NCH .. kh NCH + NCH - 1): lane fills
+  // slot lidx % CH of row lidx / CH (lidx = 64 j + lane) with the chunk the
+  // swizzle maps there; rows past the sequence end repeat its last row
   const size_t q_row = (size_t)Hq * D;
-  uint32_t qoff[NC];
+  uint32_t qoff[NCH];
 #pragma unroll
-  for (int j = 0; j < NC; ++j) {
-    const int lidx = j * 64 + lane;
+  for (int jj = 0; jj < NCH; ++jj) {
+    const int lidx = (kh * NCH + jj) * 64 + lane;
     const int r = lidx / CH;
     const int slot = lidx % CH;
-    qoff[j] = (uint32_t)(((size_t)r * q_row + 8 * (slot ^ TL::swz(r))) * 2);
+    qoff[jj] = (uint32_t)(((size_t)r * q_row + 8 * (slot ^ TL::swz(r))) * 2);
   }
-  // LSE (lanes 0-7) and Delta (lanes 8-15) of the tile's 32 rows: 16 bytes
-  // each from the padded stats rows
+  // LSE (lanes 0-7) and Delta (lanes 8-15) of the tile's 32 rows, copied by
+  // the pair's first wave
   const uint32_t st_lane = (uint32_t)(((lane >= 8 ? (size_t)Hq * a.t_pad : 0) + 4 * (lane & 7)) * 4);
   auto load_tile = [&](int i, int buf) {
-    const int st = wave + 4 * i;
+    const int st = pr + 4 * i;
     const int h = g * G + st / nq;
     const int q0 = (qt0 + st % nq) * QT;
     const bool full = q0 + QT <= L;
     const char* qsrc = (const char*)(a.q16 + ((size_t)(s0 + q0) * Hq + h) * D);
     const char* dsrc = (const char*)(a.do16 + ((size_t)(s0 + q0) * Hq + h) * D);
 #pragma unroll
-    for (int j = 0; j < NC; ++j) {
-      uint32_t off = qoff[j];
+    for (int jj = 0; jj < NCH; ++jj) {
+      const int j = kh * NCH + jj;
+      uint32_t off = qoff[jj];
       if (!full) {
         const int r = (j * 64 + lane) / CH;
         const int rr = q0 + r < L ? r : L - 1 - q0;
@@ -256,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
       dma16_to_lds_asm(qsrc, off, (buf ? qaddr1 : qaddr0) + j * 1024);
       dma16_to_lds_asm(dsrc, off, (buf ? daddr1 : daddr0) + j * 1024);
     }
-    if (lane < 16)
+    if (kh == 0 && lane < 16)
       dma16_to_lds_asm(a.stats, st_lane + (uint32_t)(((size_t)h * a.t_pad + s0 + q0) * 4), buf ? saddr1 : saddr0);
   };
 
@@ -271,43 +288,52 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
 
   if (n_mine > 0) load_tile(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();   // the K/V block copied by all four waves
+  __syncthreads();   // K, V of the block and every pair's first tile are in LDS
 
-  // the 32 keys' K and V operands stay in registers for the whole loop
-  // (lane: key lane%32, d = 16 kk + 8 half + 0..7)
-  u32x4 kreg[NKK], vreg[NKK];
+  // this wave's 32 keys' V operands stay in registers (lane: key lane%32,
+  // d = 16 kk + 8 half + 0..7); the barrier after the reads frees q_lds1
+  u32x4 vreg[NKK];
+  const int kr_l = 32 * kh + (lane & 31);            // this lane's key row in the block
+  {
+    const MIATTN_LDS uint8_t* v_l = (const MIATTN_LDS uint8_t*)q_lds1;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) vreg[kk] = lds_ld16(v_l + kr_l * (2 * D) + 16 * ((2 * kk + half) ^ TL::swz(kr_l)));
+  }
+  __syncthreads();
+
+  // LDS operand addresses: a per-lane part plus a per-lane XOR term against a
+  // compile-time offset. The swizzle of a row depends on its low bits only,
+  // so K rows 32 kh + r share Q's terms. Operand reads: chunk 2 kk + half of
+  // row r is 32 (kk ^ (sw >> 1)) + 16 (half ^ (sw & 1)). Transposing reads:
+  // rows r0 = 16 u + 4 (bb / 2) + kq / 4 and r0 + 8, chunk 4 dt + c0; with
+  // sw(r0) = 4 ta + tb (ta the same for both rows) the chunk's slot is
+  // 4 (dt ^ ta) + (c0 ^ tb).
+  uint32_t n_lane, n_x, k_lane, t_lane0, t_lane1, t_x;
   {
     const int r = lane & 31;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int o = r * (2 * D) + 16 * ((2 * kk + half) ^ TL::swz(r));
-      kreg[kk] = lds_ld16(k_l + o);
-      vreg[kk] = lds_ld16(v_l + o);
-    }
+    const int sw = TL::swz(r);
+    n_lane = (uint32_t)(r * (2 * D) + 16 * (half ^ (sw & 1)));
+    k_lane = (uint32_t)(kr_l * (2 * D) + 16 * (half ^ (sw & 1)));
+    n_x = (uint32_t)(32 * (sw >> 1));
+    const int r0 = 4 * (bb >> 1) + (kq >> 2), r1 = r0 + 8;
+    const int c0 = 2 * (bb & 1) + ((kq & 3) >> 1);
+    const int sub = 8 * (kq & 1);
+    const int s0w = TL::swz(r0), s1w = TL::swz(r1);
+    t_lane0 = (uint32_t)(r0 * (2 * D) + 16 * (c0 ^ (s0w & 3)) + sub);
+    t_lane1 = (uint32_t)(r1 * (2 * D) + 16 * (c0 ^ (s1w & 3)) + sub);
+    t_x = (uint32_t)(64 * (s0w >> 2));
   }
-
   // one loop body for both buffers (a copy per buffer would give the
   // accumulators a different register home in each and copies between them)
-  for (int i = 0; i < n_mine; ++i) {
+  for (int i = 0; i < n_iter; ++i) {
     const int buf = i & 1;
-    if (i + 1 < n_mine) load_tile(i + 1, buf ^ 1);
+    const int st = pr + 4 * i;
+    const int q0 = (qt0 + st % nq) * QT;
+    // a causal step whose queries all precede this wave's keys adds nothing
+    const bool work = i < n_mine && !(CAUSAL && q0 + QT <= kw0);
     const MIATTN_LDS uint8_t* ql = (const MIATTN_LDS uint8_t*)(uintptr_t)(buf ? qaddr1 : qaddr0);
     const MIATTN_LDS uint8_t* dl_ = (const MIATTN_LDS uint8_t*)(uintptr_t)(buf ? daddr1 : daddr0);
     const MIATTN_LDS float* sl = (const MIATTN_LDS float*)(uintptr_t)(buf ? saddr1 : saddr0);
-    const int st = wave + 4 * i;
-    const int q0 = (qt0 + st % nq) * QT;
-    // this lane's 16 rows: 8 (e/4) + 4 half + e%4
-    float l2[16], dl[16];
-#pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      const f32x4 lv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sl + 8 * gi + 4 * half);
-      const f32x4 dv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sl + 32 + 8 * gi + 4 * half);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        l2[4 * gi + e] = lv[e];
-        dl[4 * gi + e] = dv[e];
-      }
-    }
     // S = Q K^T and dP = dO V^T: A = row lane%32 of the tile, chunk 2 kk + half
     f32x16 s, dp;
 #pragma unroll
@@ -315,121 +341,126 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_kernel(BwdArgs a) {
       s[r] = 0.f;
       dp[r] = 0.f;
     }
-    {
-      // operands of step kk + 1 are read while step kk's products issue
-      const int r = lane & 31;
-      auto so = [&](int kk) { return r * (2 * D) + 16 * ((2 * kk + half) ^ TL::swz(r)); };
-      u32x4 oq = lds_ld16(ql + so(0)), od = lds_ld16(dl_ + so(0));
+    if (work) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        u32x4 nq = oq, nd = od;
-        if (kk + 1 < NKK) {
-          nq = lds_ld16(ql + so(kk + 1));
-          nd = lds_ld16(dl_ + so(kk + 1));
+        const uint32_t x = ((uint32_t)(32 * kk)) ^ n_x;
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(lds_ld16(ql + n_lane + x)), as_f16x8(lds_ld16(k_l + k_lane + x)), s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(lds_ld16(dl_ + n_lane + x)), as_f16x8(vreg[kk]), dp, 0, 0, 0);
+      }
+    }
+    // The next step's copies go out after the products above: at head_dim
+    // 128 the kernel runs at the 256-register limit with a few values
+    // spilled, and a reload of one waits for every memory load issued before
+    // it, copies included.
+    if (i + 1 < n_mine) load_tile(i + 1, buf ^ 1);
+    if (work) {
+      // P = exp2(s c - lse2) and dS = P (dP - Delta), 0 outside the sequence
+      // and (causal) above the diagonal: a masked score becomes -inf, so P = 0
+      // (a row's LSE in log2 units is finite, or +inf for a row that saw no
+      // key) and dS = 0 (dP and Delta finite); rows past the sequence end,
+      // whose stats rows may hold anything, take LSE = Delta = 0
+      const bool need_mask = kw0 + 32 > L || q0 + QT > L || (CAUSAL && kw0 + 31 > q0);
+      if (need_mask) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int qrow = q0 + 8 * (e >> 2) + 4 * half + (e & 3);
+          const bool okm = key_ok & (qrow < L) & (!CAUSAL | (key <= qrow));
+          s[e] = okm ? s[e] : kNegInf;
         }
-        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(oq), as_f16x8(kreg[kk]), s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(od), as_f16x8(vreg[kk]), dp, 0, 0, 0);
-        oq = nq; od = nd;
+      }
+      const bool tail = q0 + QT > L;
+      u32x4 pw[2], dsw[2];
+      // this lane's 16 rows: 8 (e/4) + 4 half + e%4, four at a time
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        f32x4 lv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sl + 8 * gi + 4 * half);
+        f32x4 dv = *reinterpret_cast<const MIATTN_LDS f32x4*>(sl + 32 + 8 * gi + 4 * half);
+        if (tail) {
+          const int rem = L - (q0 + 8 * gi + 4 * half);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lv[e] = e < rem ? lv[e] : 0.f;
+            dv[e] = e < rem ? dv[e] : 0.f;
+          }
+        }
+#pragma unroll
+        for (int e1 = 0; e1 < 4; e1 += 2) {
+          const int e0 = 4 * gi + e1;
+          const float p0 = exp2_hw(__builtin_fmaf(s[e0], c, -lv[e1]));
+          const float p1 = exp2_hw(__builtin_fmaf(s[e0 + 1], c, -lv[e1 + 1]));
+          pw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(p0, p1);
+          dsw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(p0 * (dp[e0] - dv[e1]), p1 * (dp[e0 + 1] - dv[e1 + 1]));
+        }
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS; X^T rows through the transposing
+      // read: block bb of 16 lanes reads rows 16 u + 4 (bb / 2) + {0..3} (+8),
+      // columns 32 dt + 16 (bb % 2) + {0..15}
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          const uint32_t x = ((uint32_t)(64 * dt)) ^ t_x;
+          const uint32_t u0 = 16 * u * (2 * D);
+          const f16x8 dot = as_f16x8(lds_ld_tr16(dl_ + t_lane0 + u0 + x), lds_ld_tr16(dl_ + t_lane1 + u0 + x));
+          const f16x8 qtr = as_f16x8(lds_ld_tr16(ql + t_lane0 + u0 + x), lds_ld_tr16(ql + t_lane1 + u0 + x));
+          dv_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(dot, as_f16x8(pw[u]), dv_acc[dt], 0, 0, 0);
+          dk_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qtr, as_f16x8(dsw[u]), dk_acc[dt], 0, 0, 0);
+        }
       }
     }
-    // P = exp2(s c - lse2) and dS = P (dP - Delta), both 0 outside the
-    // sequence and (causal) above the diagonal; only tail and diagonal
-    // tiles need the mask (uniform test)
-    // The mask goes on the inputs of the exponential, before it, so the
-    // branch does not split the vector work from the products below: a masked
-    // element gets s = -inf and zero LSE and Delta (rows past the sequence end
-    // read stats rows that may hold anything), hence P = 0 and dS =
-    // 0 * dP = 0 (masked rows and keys repeat finite Q/dO/K/V rows).
-    const bool need_mask = kb0 + 32 > L || q0 + QT > L || (CAUSAL && kb0 + 31 > q0);
-    if (need_mask) {
-      asm volatile("" ::: "memory");   // keep this a branch: the common tile skips it
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int qrow = q0 + 8 * (e >> 2) + 4 * half + (e & 3);
-        const bool ok = key_ok & (qrow < L) & (!CAUSAL | (key <= qrow));
-        s[e] = ok ? s[e] : kNegInf;
-        l2[e] = ok ? l2[e] : 0.f;
-        dl[e] = ok ? dl[e] : 0.f;
-      }
-    }
-    float p[16], d[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      p[e] = exp2_hw(__builtin_fmaf(s[e], c, -l2[e]));
-      d[e] = p[e] * (dp[e] - dl[e]);
-    }
-    u32x4 pw[2], dsw[2];
-#pragma unroll
-    for (int e0 = 0; e0 < 16; e0 += 2) {
-      pw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(p[e0], p[e0 + 1]);
-      dsw[e0 >> 3][(e0 >> 1) & 3] = pack_f16x2(d[e0], d[e0 + 1]);
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS; X^T rows through the transposing
-    // read: block bb of 16 lanes reads rows 16u + 4(bb/2) + {0..3} (+8),
-    // columns 32 dt + 16 (bb%2) + {0..15}
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int r0 = 16 * u + 4 * (bb >> 1) + (kq >> 2);
-      const int r1 = r0 + 8;
-#pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) {
-        const int col = 32 * dt + 16 * (bb & 1) + 4 * (kq & 3);
-        const int ch = col >> 3, sub = (col & 7) * 2;
-        const int o0 = r0 * (2 * D) + 16 * (ch ^ TL::swz(r0)) + sub;
-        const int o1 = r1 * (2 * D) + 16 * (ch ^ TL::swz(r1)) + sub;
-        const f16x8 dot = as_f16x8(lds_ld_tr16(dl_ + o0), lds_ld_tr16(dl_ + o1));
-        const f16x8 qtr = as_f16x8(lds_ld_tr16(ql + o0), lds_ld_tr16(ql + o1));
-        dv_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(dot, as_f16x8(pw[u]), dv_acc[dt], 0, 0, 0);
-        dk_acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qtr, as_f16x8(dsw[u]), dk_acc[dt], 0, 0, 0);
-      }
-    }
-    // this wave's copies for step i+1 have landed (each lane waits for its
-    // own; the wave's lanes run in lockstep, so the whole tile is there)
+    // this wave's copies for step i + 1 have landed; the barrier publishes
+    // both halves and closes the reads of buffer buf
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
-  // sum the four waves' partials in wave order: wave w's dK^T / dV^T go to
-  // [key][d] fp32 in the tile arrays (dK: q_lds, dV: d_lds; waves 0-1 in
-  // buffer 0, 2-3 in buffer 1)
-  __syncthreads();
-  {
-    MIATTN_LDS float* kp = (MIATTN_LDS float*)(wave < 2 ? q_lds0 : q_lds1) + (wave & 1) * QT * D;
-    MIATTN_LDS float* vp = (MIATTN_LDS float*)(wave < 2 ? d_lds0 : d_lds1) + (wave & 1) * QT * D;
-    const int kr = lane & 31;
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = 32 * dt + 8 * r4 + 4 * half;
-        f32x4 wk = {dk_acc[dt][4 * r4], dk_acc[dt][4 * r4 + 1], dk_acc[dt][4 * r4 + 2], dk_acc[dt][4 * r4 + 3]};
-        f32x4 wv = {dv_acc[dt][4 * r4], dv_acc[dt][4 * r4 + 1], dv_acc[dt][4 * r4 + 2], dv_acc[dt][4 * r4 + 3]};
-        *reinterpret_cast<MIATTN_LDS f32x4*>(kp + kr * D + d0) = wk;
-        *reinterpret_cast<MIATTN_LDS f32x4*>(vp + kr * D + d0) = wv;
-      }
-  }
-  __syncthreads();
+  // the four partials of key half 0, then of half 1, added in pair order:
+  // pair p's dK^T / dV^T go to [key][d] fp32 in the tile arrays (dK: q_lds,
+  // dV: d_lds; pairs 0-1 in buffer 0, 2-3 in buffer 1)
   const float sc = a.scale;
-  for (int idx = threadIdx.x; idx < QT * (D / 4); idx += 256) {
-    const int kr = idx / (D / 4);
-    const int d0 = 4 * (idx % (D / 4));
-    const int kk_ = kb0 + kr;
-    if (kk_ >= L) continue;
-    const int eo = kr * D + d0;
-    const f32x4 k0 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds0 + eo);
-    const f32x4 k1 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds0 + QT * D + eo);
-    const f32x4 k2 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds1 + eo);
-    const f32x4 k3 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds1 + QT * D + eo);
-    const f32x4 v0 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds0 + eo);
-    const f32x4 v1 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds0 + QT * D + eo);
-    const f32x4 v2 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds1 + eo);
-    const f32x4 v3 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds1 + QT * D + eo);
-    const f32x4 ks = (((k0 + k1) + k2) + k3) * sc;
-    const f32x4 vs = ((v0 + v1) + v2) + v3;
-    const size_t go = ((size_t)(s0 + kk_) * Hkv + g) * D + d0;
-    u32x2 wk = {pack_bf16x2(ks[0], ks[1]), pack_bf16x2(ks[2], ks[3])};
-    u32x2 wv = {pack_bf16x2(vs[0], vs[1]), pack_bf16x2(vs[2], vs[3])};
-    *reinterpret_cast<u32x2*>(a.dk + go) = wk;
-    *reinterpret_cast<u32x2*>(a.dv + go) = wv;
+#pragma unroll 1
+  for (int rnd = 0; rnd < 2; ++rnd) {
+    if (rnd > 0) __syncthreads();   // half 0's sums have been read
+    if (kh == rnd) {
+      MIATTN_LDS float* kp = (MIATTN_LDS float*)(pr < 2 ? q_lds0 : q_lds1) + (pr & 1) * QT * D;
+      MIATTN_LDS float* vp = (MIATTN_LDS float*)(pr < 2 ? d_lds0 : d_lds1) + (pr & 1) * QT * D;
+      const int kr = lane & 31;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = 32 * dt + 8 * r4 + 4 * half;
+          f32x4 wk = {dk_acc[dt][4 * r4], dk_acc[dt][4 * r4 + 1], dk_acc[dt][4 * r4 + 2], dk_acc[dt][4 * r4 + 3]};
+          f32x4 wv = {dv_acc[dt][4 * r4], dv_acc[dt][4 * r4 + 1], dv_acc[dt][4 * r4 + 2], dv_acc[dt][4 * r4 + 3]};
+          *reinterpret_cast<MIATTN_LDS f32x4*>(kp + kr * D + d0) = wk;
+          *reinterpret_cast<MIATTN_LDS f32x4*>(vp + kr * D + d0) = wv;
+        }
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < QT * (D / 4); idx += 512) {
+      const int kr = idx / (D / 4);
+      const int d0 = 4 * (idx % (D / 4));
+      const int kk_ = kb0 + 32 * rnd + kr;
+      if (kk_ >= L) continue;
+      const int eo = kr * D + d0;
+      const f32x4 k0 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds0 + eo);
+      const f32x4 k1 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds0 + QT * D + eo);
+      const f32x4 k2 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds1 + eo);
+      const f32x4 k3 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)q_lds1 + QT * D + eo);
+      const f32x4 v0 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds0 + eo);
+      const f32x4 v1 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds0 + QT * D + eo);
+      const f32x4 v2 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds1 + eo);
+      const f32x4 v3 = *reinterpret_cast<const MIATTN_LDS f32x4*>((MIATTN_LDS float*)d_lds1 + QT * D + eo);
+      const f32x4 ks = (((k0 + k1) + k2) + k3) * sc;
+      const f32x4 vs = ((v0 + v1) + v2) + v3;
+      const size_t go = ((size_t)(s0 + kk_) * Hkv + g) * D + d0;
+      u32x2 wk = {pack_bf16x2(ks[0], ks[1]), pack_bf16x2(ks[2], ks[3])};
+      u32x2 wv = {pack_bf16x2(vs[0], vs[1]), pack_bf16x2(vs[2], vs[3])};
+      *reinterpret_cast<u32x2*>(a.dk + go) = wk;
+      *reinterpret_cast<u32x2*>(a.dv + go) = wv;
+    }
   }
 }
 
@@ -462,7 +493,8 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_d256_kernel(BwdArgs a)
   constexpr int NKS = D / 32;                        // 16x16x32 steps over the head dim
   constexpr int NDB = D / 16;                        // 16-row blocks of dK^T / dV^T
   static_assert(NC % 4 == 0, "copies must split over the four waves");
-  // separate LDS objects per buffer, as in the kernel above
+  // separate LDS objects per buffer, so that a copy in flight into one does
+  // not hold up reads of another
   __shared__ __attribute__((aligned(1024))) uint8_t q_lds0[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t q_lds1[TILE];
   __shared__ __attribute__((aligned(1024))) uint8_t d_lds0[TILE];

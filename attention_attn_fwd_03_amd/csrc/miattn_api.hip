@@ -711,8 +711,9 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
   const long rows = (long)total_tokens * (num_q_heads + num_kv_heads);
   const int rpb = 256 / (head_dim / 8);
   const unsigned g_prep = (unsigned)((rows + rpb - 1) / rpb);
-  // head_dim 256: 64-key blocks (four waves of 16 keys)
-  a.n_kblocks = head_dim == 256 ? (max_seqlen + 63) / 64 : (max_seqlen + 31) / 32;
+  // 64-key blocks: two waves of 32 keys per SIMD (head_dim 64, 128), four
+  // waves of 16 keys (head_dim 256)
+  a.n_kblocks = (max_seqlen + 63) / 64;
   const unsigned g_dkdv = (unsigned)((long)num_kv_heads * a.n_kblocks * num_seqs);
   const int QR = 32 * (4 / a.heads_per_wg);
   a.n_qunits = (max_seqlen + QR - 1) / QR;
@@ -721,19 +722,19 @@ int miattn_attn_bwd(const void* q, const void* k, const void* v, const void* o, 
   if (head_dim == 64) {
     hipLaunchKernelGGL(miattn::miattn_bwd_prep_kernel<64>, dim3(g_prep), blk, 0, st, a);
     if (causal) {
-      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<64, true>), dim3(g_dkdv), blk, 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_pair_kernel<64, true>), dim3(g_dkdv), dim3(512), 0, st, a);
       hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<64, 2, true>), dim3(g_dq), blk, 0, st, a);
     } else {
-      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<64, false>), dim3(g_dkdv), blk, 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_pair_kernel<64, false>), dim3(g_dkdv), dim3(512), 0, st, a);
       hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<64, 2, false>), dim3(g_dq), blk, 0, st, a);
     }
   } else if (head_dim == 128) {
     hipLaunchKernelGGL(miattn::miattn_bwd_prep_kernel<128>, dim3(g_prep), blk, 0, st, a);
     if (causal) {
-      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<128, true>), dim3(g_dkdv), blk, 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_pair_kernel<128, true>), dim3(g_dkdv), dim3(512), 0, st, a);
       hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<128, 2, true>), dim3(g_dq), blk, 0, st, a);
     } else {
-      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_kernel<128, false>), dim3(g_dkdv), blk, 0, st, a);
+      hipLaunchKernelGGL((miattn::miattn_bwd_dkdv_pair_kernel<128, false>), dim3(g_dkdv), dim3(512), 0, st, a);
       hipLaunchKernelGGL((miattn::miattn_bwd_dq_kernel<128, 2, false>), dim3(g_dq), blk, 0, st, a);
     }
   } else {

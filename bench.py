@@ -409,7 +409,7 @@ TRAFFIC_KERNELS = {
     "decode_long_ctx131072": ("long", ["miattn_decode_split_kernel", "miattn_combine_kernel"]),
     "chunked_prefill_8x1024": ("chunked", ["miattn_prefill_fwd_kernel"]),
     "varlen_prefill_d256": ("varlen", ["miattn_prefill_pair_kernel", "miattn_bf16_to_f16_kernel"]),
-    "backward_causal_gqa_s4096": ("backward", ["miattn_bwd_prep_kernel", "miattn_bwd_dkdv_kernel",
+    "backward_causal_gqa_s4096": ("backward", ["miattn_bwd_prep_kernel", "miattn_bwd_dkdv_pair_kernel",
                                                "miattn_bwd_dq_kernel"]),
 }
 
