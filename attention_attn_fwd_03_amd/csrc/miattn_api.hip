@@ -407,7 +407,8 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
   a.c = c;
   a.seq_lens_k = nullptr; a.block_table = nullptr; a.max_pages = 0; a.num_pages = 0;
   bool pp = fwd_pingpong(head_dim, false);
-  long grid = fwd_setup(a, num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim, pp);
+  // head_dim 256 (pair kernel): one query tile per work item
+  long grid = fwd_setup(a, num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim, pp, head_dim == 256);
   if (pp && grid < kCUs) {
     pp = false;
     grid = fwd_setup(a, num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim, pp);
@@ -437,8 +438,8 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
       else launch_fwd_c<128, fwd_qb(128), 2, false, false>(a, (int)grid, cz, st);
       break;
     default:
-      // head_dim 256: the head dimension split over pairs of waves (same
-      // grid and work items as the four-wave kernel)
+      // head_dim 256: pairs of specialised waves, one query tile per
+      // workgroup
       if (cz)
         hipLaunchKernelGGL((miattn::miattn_prefill_pair_kernel<true>), dim3((unsigned)grid), dim3(512), 0, st, a);
       else

@@ -55,7 +55,7 @@ struct FwdArgs {
   int num_kv_heads;
   int group;                  // G
   int heads_per_wg;           // NH
-  int n_pairs;                // grid units per sequence: query-tile pairs (paged: query tiles)
+  int n_pairs;                // grid units per sequence: query-tile pairs (paged, head_dim 256: query tiles)
   int n_head_slots;           // Hkv * G / NH
   float c;                    // scale * log2(e)
   // paged K/V (chunked prefill): key count per sequence and page table

@@ -11,15 +11,19 @@
 //  * the output wave holds O, the running max and sum: it takes tile t - 1's
 //    scores from LDS, masks them, applies the lazy rescale, forms P and
 //    accumulates O^T += V^T P^T (16 MFMAs).
-// Phase k of the loop runs the score wave on tile k and the output wave on
-// tile k - 1, with a workgroup barrier after each phase, so on every SIMD
-// one wave's exponentials overlap the other's matrix-core work. Both waves
-// fit two per SIMD (about 110 and 180 registers). The copies of K(k + 1) and
-// V(k) into LDS are issued in phase k (K and V tiles double-buffered, the
-// score exchange too). Scores, softmax rule, rounding and accumulation
-// orders are those of the four-wave kernel (prefill.h), so the results are
-// the same bits. P.V runs on fp16 operands: V is converted to fp16
-// beforehand and the probabilities are rounded to fp16.
+// Phase k of the loop runs the score wave on the k-th key tile of the walk
+// and the output wave on the one before, with a workgroup barrier after each
+// phase, so on every SIMD one wave's exponentials overlap the other's
+// matrix-core work. Both waves fit two per SIMD (about 110 and 180
+// registers). The copies of the next phase's K tile and this phase's V tile
+// into LDS are issued in phase k (K and V tiles double-buffered, the score
+// exchange too). A workgroup takes one query tile, the heaviest first, and
+// walks its key tiles downwards from the diagonal (see the work-item note
+// below). Scores, softmax rule and roundings are those of the four-wave
+// kernel (prefill.h); the online softmax visits the key tiles in the other
+// order, which changes the result only by rounding. P.V runs on fp16
+// operands: V is converted to fp16 beforehand and the probabilities are
+// rounded to fp16.
 #pragma once
 #include <type_traits>
 
@@ -55,11 +59,17 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pair_kernel(FwdArgs a) 
   const int WQ = 4 / NH;
   const int QR = 32 * WQ;   // query rows per tile
 
-  // --- work item: (head slot, tile pair, sequence); head slot fastest ------
+  // --- work item: (head slot, query tile, sequence); head slot fastest -----
+  // One query tile per workgroup, the heaviest (causal: the last) first, and
+  // all tiles of one sequence before the next: the workgroups dealt to an XCD
+  // together start together and walk the same key tiles at the same time, so
+  // one kv head's K/V is read from L2 by all of them (causal pairs of tiles
+  // put the resident workgroups at different key positions, and the K/V of a
+  // long sequence, 7.5 MB per head at 7K tokens, does not fit an XCD's L2).
   const int lin = blockIdx.x;
   const int hslot = lin % a.n_head_slots;
   const int rest = lin / a.n_head_slots;
-  const int pair = rest % a.n_pairs;
+  const int unit = rest % a.n_pairs;
   const int b = rest / a.n_pairs;
   int s0 = a.cu_seqlens[b];
   int s1 = a.cu_seqlens[b + 1];
@@ -67,9 +77,8 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pair_kernel(FwdArgs a) 
   s1 = s1 < s0 ? s0 : (s1 > a.total_tokens ? a.total_tokens : s1);
   const int L = s1 - s0;
   const int n_tiles = (L + QR - 1) / QR;
-  // query tiles i and n-1-i together cost the same for every pair (causal)
-  if (pair > n_tiles - 1 - pair) return;   // uniform over the workgroup
-  const int n_mine = pair != n_tiles - 1 - pair ? 2 : 1;
+  if (unit >= n_tiles) return;   // uniform over the workgroup
+  const int qt = n_tiles - 1 - unit;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -126,14 +135,19 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pair_kernel(FwdArgs a) 
   const int bb = lane >> 4, kq = lane & 15;
   const int r_k = lane & 31;   // K row this lane reads as the A operand
 
-  for (int tsel = 0; tsel < n_mine; ++tsel) {
-    const int qt = tsel == 0 ? pair : n_tiles - 1 - pair;
+  {
     const int q0 = qt * QR + 32 * qs;   // first query row of this block
     const int qt_end = qt * QR + QR;
     const int kend_wg = CAUSAL ? (qt_end < L ? qt_end : L) : L;
     const int n_kt = (kend_wg + BC - 1) / BC;
     const int kend_w = CAUSAL ? (q0 + 32 < L ? q0 + 32 : L) : L;
     const int n_kt_w = q0 < L ? (kend_w + BC - 1) / BC : 0;   // tiles this block computes
+    // Key tiles are walked downwards, from the workgroup's last (the causal
+    // diagonal, or the tail) to 0: with the heaviest tiles dealt first, the
+    // workgroups resident on an XCD then move down one sequence's keys
+    // together, a few tiles apart, and share them in L2. A block's first
+    // tile always holds a key it sees. Phase k covers tile(k).
+    auto tile = [&](int k) { return n_kt - 1 - k; };
 
     // The two roles run separate loops (so neither keeps the other's
     // registers live) with the same barriers: one or two before phase 0,
@@ -154,15 +168,14 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pair_kernel(FwdArgs a) 
           qop[kk] = ok ? ld16(qp + 16 * kk) : z;
         }
       }
-      if (tsel > 0) __syncthreads();   // previous tile's last reads before the buffers are refilled
-      if (n_kt > 0) load_k(0, 0);
+      if (n_kt > 0) load_k(tile(0), 0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       auto phase = [&](int k, auto parc) {
         constexpr int par = decltype(parc)::value;   // k & 1
-        if (k + 1 < n_kt) load_k(k + 1, par ^ 1);
-        if (k < n_kt) load_v(k, par);
-        if (k < n_kt_w) {
+        if (k + 1 < n_kt) load_k(tile(k + 1), par ^ 1);
+        if (k < n_kt) load_v(tile(k), par);
+        if (k < n_kt && tile(k) < n_kt_w) {
           f32x16 s;
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[r] = 0.f;
@@ -191,16 +204,15 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pair_kernel(FwdArgs a) 
       for (int i = 0; i < NDT; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-      if (tsel > 0) __syncthreads();
-      if (n_kt > 0) load_k(0, 0);
+      if (n_kt > 0) load_k(tile(0), 0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       auto phase = [&](int k, auto parc) {
         constexpr int par = decltype(parc)::value;   // k & 1
-        if (k + 1 < n_kt) load_k(k + 1, par ^ 1);
-        if (k < n_kt) load_v(k, par);
-        const int kt = k - 1;
-        if (kt >= 0 && kt < n_kt_w) {
+        if (k + 1 < n_kt) load_k(tile(k + 1), par ^ 1);
+        if (k < n_kt) load_v(tile(k), par);
+        const int kt = tile(k - 1);   // the score wave's tile of the previous phase
+        if (k >= 1 && kt < n_kt_w) {
           const MIATTN_LDS f32x4* xi = xbuf(par ^ 1) + w4 * 256;
           f32x16 s;
 #pragma unroll
@@ -277,12 +289,21 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pair_kernel(FwdArgs a) 
       }
 
       // --- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 -------------------
+      // After the last barrier no wave reads the K/V buffers: output wave w4
+      // stages its 32 x D block of O in buffer w4 (bf16, chunk c of row r in
+      // slot c ^ (r mod 16)) and stores whole rows, 16 bytes per lane. Stored
+      // from the accumulator layout, each instruction would write 8 bytes
+      // into each of 32 rows, and lines evicted half-written cost extra
+      // write traffic.
       const float lt = l + xor32(l);
       const int qrow = q0 + (lane & 31);
-      if (qrow < L) {
-        const bool empty = !(lt > 0.f);
-        const float inv = empty ? 0.f : 1.f / lt;
-        uint16_t* op = a.o + ((size_t)(s0 + qrow) * Hq + h) * D + 4 * half;
+      const bool empty = !(lt > 0.f);
+      const float inv = empty ? 0.f : 1.f / lt;
+      static_assert(32 * D * 2 == TILE_BYTES, "one output block per K/V buffer");
+      MIATTN_LDS uint8_t* stg = (w4 >> 1) ? vbuf(w4 & 1) : kbuf(w4 & 1);
+      {
+        const int r = lane & 31;
+        MIATTN_LDS uint8_t* sr = stg + r * (2 * D) + 8 * half;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
@@ -290,11 +311,18 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pair_kernel(FwdArgs a) 
             const f32x16& A = acc[dt];
             u32x2 w = {pack_bf16x2(A[4 * r4] * inv, A[4 * r4 + 1] * inv),
                        pack_bf16x2(A[4 * r4 + 2] * inv, A[4 * r4 + 3] * inv)};
-            *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * r4) = w;
+            *reinterpret_cast<MIATTN_LDS u32x2*>(sr + 16 * ((4 * dt + r4) ^ (r & 15))) = w;
           }
-        if (a.lse != nullptr && half == 0)
-          a.lse[(size_t)h * a.total_tokens + s0 + qrow] = empty ? kNegInf : (m + log2_hw(lt)) * kLn2;
       }
+#pragma unroll
+      for (int j = 0; j < 32 * CH / 64; ++j) {
+        const int lidx = 64 * j + lane;
+        const int r = lidx / CH, ch = lidx % CH;
+        const u32x4 w = lds_ld16(stg + r * (2 * D) + 16 * (ch ^ (r & 15)));
+        if (q0 + r < L) st16(a.o + ((size_t)(s0 + q0 + r) * Hq + h) * D + 8 * ch, w);
+      }
+      if (qrow < L && a.lse != nullptr && half == 0)
+        a.lse[(size_t)h * a.total_tokens + s0 + qrow] = empty ? kNegInf : (m + log2_hw(lt)) * kLn2;
     }
   }
 }

@@ -213,10 +213,16 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
     if (tsel > 0) __syncthreads();   // the previous tile's last reads are done
     if (n_kt > 0) copy_tile(0, kbase, koff, lds_addr(kbuf(0)));
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // The Q rows have landed (the wait above covers every load). Reading
+    // their registers here lets the compiler see that: otherwise it places
+    // its own vmcnt waits before the loop's first score products, where they
+    // would also wait for the K/V copies issued for the next tile.
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) asm volatile("" ::"v"(qop[kk]));
     __syncthreads();
 
-    // GEMM(t): P(t-1) V(t-1) into O, then S(t) = K(t) Q^T
-    auto gemm = [&](int t) __attribute__((always_inline)) {
+    // GEMM(t): P(t-1) V(t-1) into O (pv), then S(t) = K(t) Q^T (qk)
+    auto pv = [&](int t) __attribute__((always_inline)) {
       if (t >= 1 && t - 1 < n_kt_w) {
         const MIATTN_LDS uint8_t* vl = vbuf((t - 1) & 1) + v_lane;
 #pragma unroll
@@ -233,6 +239,8 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
           }
         pp_mfma_reads<KB * 2 * NDT, 2, 8>();
       }
+    };
+    auto qk = [&](int t) __attribute__((always_inline)) {
       if (t < n_kt_w) {
         const MIATTN_LDS uint8_t* kl = kbuf(t & 1) + k_lane;
 #pragma unroll
@@ -330,30 +338,36 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
     // at different points); every wave of interval i reads K(i) and V(i - 1),
     // and each wave issues its share of the copies of K(i + 1) and V(i) right
     // after the barrier that opens the interval and waits for it at its end.
-    // In the last interval (i = n_kt) no copy is in flight and Q is dead (the
-    // last S was in interval n_kt - 1): the next query tile's Q rows are
-    // loaded there and travel through the last P V and the epilogue; the
-    // next pass's first wait covers them.
+    // The last interval (i = n_kt) holds only P(n_kt - 1) V(n_kt - 1); no
+    // copy is in flight and Q is dead (the last S was in interval n_kt - 1):
+    // the next query tile's Q rows are loaded there and travel through the
+    // last P V and the epilogue; the next pass's first wait covers them. That
+    // interval sits outside the loop, so no Q load is pending inside it.
     if (grp == 1) copies(0);
-    for (int i = 0; i <= n_kt; ++i) {
-      if (i == n_kt && tsel + 1 < n_mine) load_q(tile_of(tsel + 1));
+    for (int i = 0; i < n_kt; ++i) {
       if (grp == 0) copies(i);
       // the wave in its MFMA half of the interval issues first when both
       // waves of a SIMD have an instruction ready
       __builtin_amdgcn_s_setprio(1);
-      gemm(i);
+      pv(i);
+      qk(i);
       __builtin_amdgcn_s_setprio(0);
       if (grp == 1) {
-        if (i < n_kt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         copies(i + 1);
       }
-      if (i < n_kt) soft(i);
+      soft(i);
       if (grp == 0) {
-        if (i < n_kt) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
       }
     }
+    if (tsel + 1 < n_mine) load_q(tile_of(tsel + 1));
+    __builtin_amdgcn_s_setprio(1);
+    pv(n_kt);
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();
 
     // --- epilogue: O = acc / l, LSE = (m + log2 l) ln 2 --------------------
     // After the loop's last barrier the K/V buffers are free: each wave stages
