@@ -230,8 +230,12 @@ __global__ __launch_bounds__(512, 1) void miattn_bwd_dkdv_pair_kernel(BwdArgs a)
   }
   const MIATTN_LDS uint8_t* k_l = (const MIATTN_LDS uint8_t*)k_lds;
 
-  // steps: (query head of the group, query tile); causal tiles start at the
-  // one holding query kb0; pair p takes steps p, p + 4, ...
+  // steps: (query tile, query head of the group), the last query tile first
+  // and the heads fastest, down to (causal) the tile holding query kb0; pair p
+  // takes steps p, p + 4, ... Every key block walks the same tiles in the
+  // same order, so the workgroups resident on an XCD read one query tile at a
+  // time and share it in L2 (a head-by-head walk from each block's own first
+  // tile spread them over the group's whole Q/dO, 8 MB at 4K tokens).
   const int n_qt = (L + QT - 1) / QT;
   const int qt0 = CAUSAL ? kb0 / QT : 0;
   const int nq = n_qt - qt0;
@@ -256,8 +260,8 @@ __global__ __launch_bounds__(512, 1) void miattn_bwd_dkdv_pair_kernel(BwdArgs a)
   const uint32_t st_lane = (uint32_t)(((lane >= 8 ? (size_t)Hq * a.t_pad : 0) + 4 * (lane & 7)) * 4);
   auto load_tile = [&](int i, int buf) {
     const int st = pr + 4 * i;
-    const int h = g * G + st / nq;
-    const int q0 = (qt0 + st % nq) * QT;
+    const int h = g * G + st % G;
+    const int q0 = (n_qt - 1 - st / G) * QT;
     const bool full = q0 + QT <= L;
     const char* qsrc = (const char*)(a.q16 + ((size_t)(s0 + q0) * Hq + h) * D);
     const char* dsrc = (const char*)(a.do16 + ((size_t)(s0 + q0) * Hq + h) * D);
@@ -328,7 +332,7 @@ __global__ __launch_bounds__(512, 1) void miattn_bwd_dkdv_pair_kernel(BwdArgs a)
   for (int i = 0; i < n_iter; ++i) {
     const int buf = i & 1;
     const int st = pr + 4 * i;
-    const int q0 = (qt0 + st % nq) * QT;
+    const int q0 = (n_qt - 1 - st / G) * QT;
     // a causal step whose queries all precede this wave's keys adds nothing
     const bool work = i < n_mine && !(CAUSAL && q0 + QT <= kw0);
     const MIATTN_LDS uint8_t* ql = (const MIATTN_LDS uint8_t*)(uintptr_t)(buf ? qaddr1 : qaddr0);
@@ -547,8 +551,9 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_d256_kernel(BwdArgs a)
     }
   }
 
-  // steps: (query head of the group, query tile), causal tiles from the one
-  // holding query kb0; all four waves take every step
+  // steps: (query tile, query head of the group), the last query tile first
+  // and the heads fastest, down to (causal) the tile holding query kb0; all
+  // four waves take every step (the walk order shares L2 as above)
   const int n_qt = (L + QT - 1) / QT;
   const int qt0 = CAUSAL ? kb0 / QT : 0;
   const int nq = n_qt - qt0;
@@ -568,8 +573,8 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_d256_kernel(BwdArgs a)
   }
   const uint32_t st_lane = (uint32_t)(((lane >= 8 ? (size_t)Hq * a.t_pad : 0) + 4 * (lane & 7)) * 4);
   auto load_tile = [&](int st, int buf) {
-    const int h = g * G + st / nq;
-    const int q0 = (qt0 + st % nq) * QT;
+    const int h = g * G + st % G;
+    const int q0 = (n_qt - 1 - st / G) * QT;
     const bool full = q0 + QT <= L;
     const char* qsrc = (const char*)(a.q16 + ((size_t)(s0 + q0) * Hq + h) * D);
     const char* dsrc = (const char*)(a.do16 + ((size_t)(s0 + q0) * Hq + h) * D);
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(256, 1) void miattn_bwd_dkdv_d256_kernel(BwdArgs a)
   for (int i = 0; i < n_steps; ++i) {
     const int buf = i & 1;
     if (i + 1 < n_steps) load_tile(i + 1, buf ^ 1);
-    const int q0 = (qt0 + i % nq) * QT;
+    const int q0 = (n_qt - 1 - i / G) * QT;
     // a causal step whose queries all precede this wave's keys adds nothing
     if (wave_live && (!CAUSAL || q0 + QT - 1 >= kw0)) {
       const MIATTN_LDS uint8_t* ql = (const MIATTN_LDS uint8_t*)(uintptr_t)(buf ? qaddr1 : qaddr0);

@@ -277,6 +277,8 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
       }
       // P(t) = exp2(s c - m) in bf16 and the tile's row sum ls (fp32 values,
       // summed in score order, then added to l)
+      // (the sum starts from the first pair: the probabilities are never
+      // negative, so this is the bits of 0 + ..., one add fewer)
       auto exps = [&](float nmu) __attribute__((always_inline)) {
         float ls = 0.f;
 #pragma unroll
@@ -285,7 +287,7 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
           for (int r = 0; r < 16; r += 2) {
             const float p0 = exp2_hw(__builtin_fmaf(s[kb][r], c, nmu));
             const float p1 = exp2_hw(__builtin_fmaf(s[kb][r + 1], c, nmu));
-            ls += p0 + p1;
+            ls = (kb == 0 && r == 0) ? p0 + p1 : ls + (p0 + p1);
             pw[kb][r >> 3][(r >> 1) & 3] = pack_p<F16V>(p0, p1);
           }
         return ls;
