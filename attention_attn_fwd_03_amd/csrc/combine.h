@@ -64,37 +64,53 @@ inline int combine_cols(long rows, int head_dim) {
   return cols;
 }
 
-// Grid: (rows, ceil(D / (4 cols))). Threads: cols column lanes x NG = 256 /
-// cols split groups; group g sums splits g, g + NG, ... in increasing order.
-__global__ __launch_bounds__(256) void miattn_combine_kernel(CombineArgs a) {
-  __shared__ float red[4];
-  __shared__ f32x4 part[256];
-  __shared__ float wpart[256];
-  const int row = blockIdx.x;
-  const int S = a.num_splits;
+// This row's partials: S_row of them, LSE s at pl[s * ls], output s at
+// po + s * os (the [rows][S][D] layout, or the balanced groups' layout).
+struct RowPartials {
+  int S_row;
+  const float* pl;
+  const float* po;
+  size_t ls, os;
+};
+__device__ __forceinline__ RowPartials row_partials(const CombineArgs& a, int row) {
+  RowPartials r;
+  const int D = a.head_dim;
+  r.S_row = a.num_splits;
+  r.pl = a.part_lse + (size_t)row * a.num_splits;
+  r.po = a.part_o + (size_t)row * a.num_splits * D;
+  r.ls = 1;
+  r.os = D;
+  if (a.plan_table != nullptr) {
+    const int Hq = a.num_q_heads;
+    const int b = row / Hq;
+    r.S_row = a.plan_table[a.batch + b];
+    const size_t first = (size_t)a.plan_table[b] * Hq + row % Hq;
+    r.pl = a.part_lse + first;
+    r.po = a.part_o + first * D;
+    r.ls = Hq;
+    r.os = (size_t)Hq * D;
+  }
+  return r;
+}
+
+// One output row merged by the whole workgroup (256 threads, every thread
+// must call it): ncol_max float4 columns from col0, ncol column lanes x
+// NG = 256 / ncol split groups; group g sums splits g, g + NG, ... in
+// increasing order, and the groups are folded in group order.
+__device__ __forceinline__ void combine_row_block(const CombineArgs& a, int row, int col0, int ncol_max,
+                                                  float* red, f32x4* part, float* wpart) {
   const int D = a.head_dim;
   const int DQ = D / 4;
-  const int col0 = blockIdx.y * a.cols;
-  const int ncol = DQ - col0 < a.cols ? DQ - col0 : a.cols;
+  const int ncol = DQ - col0 < ncol_max ? DQ - col0 : ncol_max;
   const int NG = 256 / ncol;
   const int t = threadIdx.x;
   const int c = col0 + t % ncol;
   const int gi = t / ncol;
-  // this row's partials: S of them, LSE s at pl[s * ls], output s at po + s * os
-  int S_row = S;
-  const float* pl = a.part_lse + (size_t)row * S;
-  const float* po = a.part_o + (size_t)row * S * D;
-  size_t ls = 1, os = D;
-  if (a.plan_table != nullptr) {
-    const int Hq = a.num_q_heads;
-    const int b = row / Hq;
-    S_row = a.plan_table[a.batch + b];
-    const size_t first = (size_t)a.plan_table[b] * Hq + row % Hq;
-    pl = a.part_lse + first;
-    po = a.part_o + first * D;
-    ls = Hq;
-    os = (size_t)Hq * D;
-  }
+  const RowPartials rp = row_partials(a, row);
+  const int S_row = rp.S_row;
+  const float* pl = rp.pl;
+  const float* po = rp.po;
+  const size_t ls = rp.ls, os = rp.os;
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
   float M, W;
@@ -173,6 +189,101 @@ __global__ __launch_bounds__(256) void miattn_combine_kernel(CombineArgs a) {
       for (int k = 1; k < NG; ++k) acc += part[k * ncol + t];
     }
   }
+  if (gi == 0) {
+    const bool empty = M == kNegInf || !(W > 0.f);
+    const f32x4 sum = empty ? z : acc * (1.f / W);
+    if (a.out_bf16) {
+      u32x2 w2 = {pack_bf16x2(sum[0], sum[1]), pack_bf16x2(sum[2], sum[3])};
+      *reinterpret_cast<u32x2*>((uint16_t*)a.o + (size_t)row * D + 4 * c) = w2;
+    } else {
+      *reinterpret_cast<f32x4*>((float*)a.o + (size_t)row * D + 4 * c) = sum;
+    }
+    if (a.lse != nullptr && c == 0) a.lse[row] = empty ? kNegInf : M + log2_hw(W) * kLn2;
+  }
+}
+
+// Grid: (rows, ceil(D / (4 cols))): one row and up to cols float4 columns
+// per workgroup.
+__global__ __launch_bounds__(256) void miattn_combine_kernel(CombineArgs a) {
+  __shared__ float red[4];
+  __shared__ f32x4 part[256];
+  __shared__ float wpart[256];
+  combine_row_block(a, blockIdx.x, blockIdx.y * a.cols, a.cols, red, part, wpart);
+}
+
+// Most splits per row that one wave merges alone in the row kernel below.
+constexpr int kCombineWaveSplits = 16;
+
+// The merge for decode rows with few splits (head_dim 64, 128 or 256): four
+// rows per workgroup, one wave per row, no barrier and no LDS. Every lane
+// reads all of its row's LSEs, so the max M and the weight sum W (added in
+// split order) need no reduction; lane l takes float4 column l mod D/4 of
+// the splits s = l / (D/4) + k (64 / (D/4)), and the split groups are folded
+// by XOR shuffles (each step adds the same two values in every lane, so all
+// lanes agree). A workgroup whose rows have more splits merges them one at a
+// time with the whole workgroup, as the kernel above does.
+template <int D>
+__global__ __launch_bounds__(256) void miattn_combine_rows_kernel(CombineArgs a) {
+  __shared__ float red[4];
+  __shared__ f32x4 part[256];
+  __shared__ float wpart[256];
+  constexpr int DQ = D / 4;
+  constexpr int NGW = 64 / DQ;                     // split groups per wave
+  constexpr int KU = kCombineWaveSplits / NGW;     // partial loads per lane
+  static_assert(64 % DQ == 0 && KU >= 1, "head_dim 64, 128 or 256");
+  const int r0 = blockIdx.x * 4;
+  // the largest split count of the workgroup's rows, read by every wave
+  // (a uniform choice without a barrier)
+  int smax = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (r0 + i < a.rows) {
+      const int sr = row_partials(a, r0 + i).S_row;
+      smax = sr > smax ? sr : smax;
+    }
+  if (smax > kCombineWaveSplits) {
+    for (int i = 0; i < 4; ++i)
+      if (r0 + i < a.rows) {
+        combine_row_block(a, r0 + i, 0, DQ, red, part, wpart);
+        __syncthreads();   // this row's fold reads are done before the next row's writes
+      }
+    return;
+  }
+  const int row = r0 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (row >= a.rows) return;
+  const int lane = threadIdx.x & 63;
+  const int c = lane % DQ, gi = lane / DQ;
+  const RowPartials rp = row_partials(a, row);
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 v[KU];
+  float x[KU];
+#pragma unroll
+  for (int u = 0; u < KU; ++u) {
+    const int s = gi + u * NGW;
+    const bool ok = s < rp.S_row;
+    x[u] = ok ? rp.pl[(size_t)s * rp.ls] : kNegInf;
+    v[u] = ok ? *reinterpret_cast<const f32x4*>(rp.po + (size_t)s * rp.os + 4 * c) : z;
+  }
+  float M = kNegInf;
+  for (int s = 0; s < rp.S_row; ++s) M = fmaxf(M, rp.pl[(size_t)s * rp.ls]);
+  float W = 0.f;
+  f32x4 acc = z;
+  if (M != kNegInf) {
+    for (int s = 0; s < rp.S_row; ++s) {
+      const float xs = rp.pl[(size_t)s * rp.ls];
+      W += (xs == kNegInf) ? 0.f : exp2_hw((xs - M) * kLog2e);
+    }
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const bool skip = x[u] == kNegInf;
+      const float w = skip ? 0.f : exp2_hw((x[u] - M) * kLog2e);
+      acc += skip ? z : w * v[u];
+    }
+  }
+#pragma unroll
+  for (int m = DQ; m < 64; m <<= 1)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] += __shfl_xor(acc[e], m);
   if (gi == 0) {
     const bool empty = M == kNegInf || !(W > 0.f);
     const f32x4 sum = empty ? z : acc * (1.f / W);

@@ -613,9 +613,21 @@ int decode_paged_impl(const char* who, const void* q, const void* k_cache, const
     if (units > 0) {
       c.plan_table = a.plan_table; c.batch = batch; c.num_q_heads = num_q_heads;
     }
-    c.cols = miattn::combine_cols((long)rows, head_dim);
-    const unsigned chunks = (unsigned)((head_dim / 4 + c.cols - 1) / c.cols);
-    hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3((unsigned)rows, chunks), dim3(256), 0, st, c);
+    if (units > 0 || S <= miattn::kCombineWaveSplits) {
+      // one wave per row (the balanced plan's per-row split counts are only
+      // known on the device; the kernel takes rows with many splits a
+      // workgroup at a time)
+      const unsigned g = (unsigned)((rows + 3) / 4);
+      switch (head_dim) {
+        case 64: hipLaunchKernelGGL(miattn::miattn_combine_rows_kernel<64>, dim3(g), dim3(256), 0, st, c); break;
+        case 128: hipLaunchKernelGGL(miattn::miattn_combine_rows_kernel<128>, dim3(g), dim3(256), 0, st, c); break;
+        default: hipLaunchKernelGGL(miattn::miattn_combine_rows_kernel<256>, dim3(g), dim3(256), 0, st, c); break;
+      }
+    } else {
+      c.cols = miattn::combine_cols((long)rows, head_dim);
+      const unsigned chunks = (unsigned)((head_dim / 4 + c.cols - 1) / c.cols);
+      hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3((unsigned)rows, chunks), dim3(256), 0, st, c);
+    }
     r = check_launch("combine");
     if (r) return r;
   }
