@@ -96,7 +96,7 @@ __device__ __forceinline__ RowPartials row_partials(const CombineArgs& a, int ro
 // One output row merged by the whole workgroup (256 threads, every thread
 // must call it): ncol_max float4 columns from col0, ncol column lanes x
 // NG = 256 / ncol split groups; group g sums splits g, g + NG, ... in
-// increasing order, and the groups are folded in group order.
+// increasing order, and the groups are folded pairwise in a fixed order.
 __device__ __forceinline__ void combine_row_block(const CombineArgs& a, int row, int col0, int ncol_max,
                                                   float* red, f32x4* part, float* wpart) {
   const int D = a.head_dim;
@@ -144,14 +144,21 @@ __device__ __forceinline__ void combine_row_block(const CombineArgs& a, int row,
     part[t] = acc;
     wpart[t] = ws;
     __syncthreads();
+    // pairwise fold of the NG groups: in each round group g < n - h adds
+    // group g + h (h = ceil(n / 2)); readers and writers never overlap
+    for (int n = NG; n > 1;) {
+      const int h = (n + 1) >> 1;
+      if (gi < n - h) {
+        part[t] += part[t + h * ncol];
+        wpart[t] += wpart[t + h * ncol];
+      }
+      n = h;
+      __syncthreads();
+    }
     W = 0.f;
     if (gi == 0) {
       acc = part[t];
       W = wpart[t];
-      for (int k = 1; k < NG; ++k) {
-        acc += part[k * ncol + t];
-        W += wpart[k * ncol + t];
-      }
     }
   } else {
     float mx = kNegInf;
@@ -184,10 +191,13 @@ __device__ __forceinline__ void combine_row_block(const CombineArgs& a, int row,
     }
     part[t] = acc;
     __syncthreads();
-    if (gi == 0) {
-      acc = part[t];
-      for (int k = 1; k < NG; ++k) acc += part[k * ncol + t];
+    for (int n = NG; n > 1;) {   // the pairwise fold above
+      const int h = (n + 1) >> 1;
+      if (gi < n - h) part[t] += part[t + h * ncol];
+      n = h;
+      __syncthreads();
     }
+    if (gi == 0) acc = part[t];
   }
   if (gi == 0) {
     const bool empty = M == kNegInf || !(W > 0.f);

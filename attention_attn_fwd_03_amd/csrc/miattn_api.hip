@@ -523,6 +523,27 @@ namespace {
 // Where the decode's split partials live.
 enum class WsMode { kCaller, kStaticScratch };
 
+// The merge of a decode's split partials (head_dim 64, 128 or 256): one wave
+// per row for the balanced groups (whose per-row split counts are only known
+// on the device; the kernel merges rows with many splits a workgroup at a
+// time) and for up to kCombineWaveSplits contiguous splits, the block form
+// for more. The numerics entry's LSE record takes the same choice, so it
+// gives the fast path's bits.
+void launch_decode_merge(miattn::CombineArgs& c, hipStream_t st) {
+  if (c.plan_table != nullptr || c.num_splits <= miattn::kCombineWaveSplits) {
+    const unsigned g = (unsigned)((c.rows + 3) / 4);
+    switch (c.head_dim) {
+      case 64: hipLaunchKernelGGL(miattn::miattn_combine_rows_kernel<64>, dim3(g), dim3(256), 0, st, c); break;
+      case 128: hipLaunchKernelGGL(miattn::miattn_combine_rows_kernel<128>, dim3(g), dim3(256), 0, st, c); break;
+      default: hipLaunchKernelGGL(miattn::miattn_combine_rows_kernel<256>, dim3(g), dim3(256), 0, st, c); break;
+    }
+  } else {
+    c.cols = miattn::combine_cols((long)c.rows, c.head_dim);
+    const unsigned chunks = (unsigned)((c.head_dim / 4 + c.cols - 1) / c.cols);
+    hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3((unsigned)c.rows, chunks), dim3(256), 0, st, c);
+  }
+}
+
 int decode_paged_impl(const char* who, const void* q, const void* k_cache, const void* v_cache,
                       const int32_t* block_table, const int32_t* seq_lens, int batch, int max_pages_per_seq,
                       int page_size, int num_pages, int num_q_heads, int num_kv_heads, int head_dim, float scale,
@@ -613,21 +634,7 @@ int decode_paged_impl(const char* who, const void* q, const void* k_cache, const
     if (units > 0) {
       c.plan_table = a.plan_table; c.batch = batch; c.num_q_heads = num_q_heads;
     }
-    if (units > 0 || S <= miattn::kCombineWaveSplits) {
-      // one wave per row (the balanced plan's per-row split counts are only
-      // known on the device; the kernel takes rows with many splits a
-      // workgroup at a time)
-      const unsigned g = (unsigned)((rows + 3) / 4);
-      switch (head_dim) {
-        case 64: hipLaunchKernelGGL(miattn::miattn_combine_rows_kernel<64>, dim3(g), dim3(256), 0, st, c); break;
-        case 128: hipLaunchKernelGGL(miattn::miattn_combine_rows_kernel<128>, dim3(g), dim3(256), 0, st, c); break;
-        default: hipLaunchKernelGGL(miattn::miattn_combine_rows_kernel<256>, dim3(g), dim3(256), 0, st, c); break;
-      }
-    } else {
-      c.cols = miattn::combine_cols((long)rows, head_dim);
-      const unsigned chunks = (unsigned)((head_dim / 4 + c.cols - 1) / c.cols);
-      hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3((unsigned)rows, chunks), dim3(256), 0, st, c);
-    }
+    launch_decode_merge(c, st);
     r = check_launch("combine");
     if (r) return r;
   }
@@ -842,10 +849,9 @@ int miattn_attn_decode_paged_numerics(const void* q, const void* k_cache, const 
   const unsigned chunks = (unsigned)((head_dim / 4 + cols - 1) / cols);
   if (record == 0) {
     miattn::CombineArgs c{};
-    c.cols = cols;
     c.part_o = a.part_o; c.part_lse = a.part_lse; c.o = o; c.lse = lse;
     c.rows = (int)rows; c.num_splits = S; c.head_dim = head_dim; c.out_bf16 = out_dtype == MIATTN_BF16;
-    hipLaunchKernelGGL(miattn::miattn_combine_kernel, dim3((unsigned)rows, chunks), dim3(256), 0, st, c);
+    launch_decode_merge(c, st);
   } else {
     miattn::MergeStatsArgs m{};
     m.part_o = a.part_o; m.part_m = a.part_m; m.part_l = a.part_l; m.o = o; m.lse = lse;
