@@ -219,7 +219,8 @@ int miattn_attn_decode_paged_noalloc(const void* q, const void* k_cache, const v
  * section "Backend names expand into four decode algorithms"):
  *     M = max_s LSE_s over non-empty splits, w_s = exp(LSE_s - M),
  *     O = sum_s w_s O_s / sum_s w_s,   LSE = M + ln sum_s w_s,
- * splits taken in the fixed order s = 0 .. num_splits-1. A split with
+ * the sums taken in one fixed order (strided groups of splits, then a
+ * pairwise fold of the groups), so the result is bitwise repeatable. A split with
  * LSE_s = -inf is empty and skipped; a row whose splits are all empty gives
  * O = 0, LSE = -inf.
  *   partial_o   [rows, num_splits, D] float32 (normalised partial outputs)
