@@ -289,3 +289,26 @@ def test_policy_small_launch_contiguous_within_workspace_bound():
     assert_lse_close(host(lc), L, "small launch, caller workspace")
     ol, ll = run(case, 0, dev)
     assert bitwise_equal(oc, ol) and bitwise_equal(lc, ll)
+
+
+def test_policy_groups_long_rows_beside_short_ones():
+    # length-proportional groups where one sequence takes far more than the
+    # 16 splits one wave merges alone (about 80 groups) beside short and empty
+    # ones, with 6 query heads per sequence so that some merge workgroups' four
+    # rows belong to two sequences: those merge row by row with the whole
+    # workgroup, the rest one wave per row
+    lens = [40000, 100, 3000, 17, 0, 20000] * 2
+    case = synth.make_decode(3, 17, lens, 6, 2, 128, 1 / math.sqrt(128), shuffle=True, tail="nan",
+                             name="policy_long_rows")
+    assert mi.decode_pick_splits(case.batch, 2, case.max_pages * 16) > 1
+    assert case.batch * case.max_pages * 16 >= 1 << 17
+    dev = to_dev(case)
+    O, L = reference(case)
+    o1, l1 = run(case, 0, dev)
+    assert_bf16_close(host(o1), O, "policy groups, long rows")
+    assert_lse_close(host(l1), L, "policy groups, long rows")
+    o2, l2 = run(case, 0, dev)
+    assert bitwise_equal(o1, o2) and bitwise_equal(l1, l2)
+    o4, _ = run(case, 4, dev)
+    mx, mean = errors(host(o1), host(o4))
+    assert mx <= 1e-2 and mean <= 1e-3
