@@ -79,6 +79,11 @@ __device__ __forceinline__ int lane_id() {
 // 16-byte global load / store through plain vector types.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+// Non-temporal 16-byte store for output no kernel of the call reads back
+// (keeps it from displacing K/V tiles in L2).
+__device__ __forceinline__ void st16_stream(void* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 // Non-temporal 16-byte load for data that is read exactly once.
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
@@ -150,6 +155,14 @@ __device__ __forceinline__ f32x16 mfma_pv(u32x2 lo, u32x2 hi, u32x4 p, f32x16 ac
 // group per thread and grid stride: exact for magnitudes in [2^-14, 65504];
 // smaller ones become fp16 subnormals (absolute error at most 2^-25), larger
 // ones overflow to inf.
+// Words of a work queue: per-XCD counters and an exit count.
+constexpr int kWorkQueueWords = 9;
+
+// Sets n words to zero (the work queues' first initialisation).
+__global__ __launch_bounds__(64) void miattn_zero_u32_kernel(unsigned* p, int n) {
+  for (int i = threadIdx.x; i < n; i += 64) p[i] = 0u;
+}
+
 __global__ __launch_bounds__(256) void miattn_bf16_to_f16_kernel(const uint16_t* __restrict__ src,
                                                                  uint16_t* __restrict__ dst, long n8) {
   for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n8; i += (long)gridDim.x * 256)

@@ -60,6 +60,7 @@ int g_arch_ok[kMaxDevices];          // 0 unknown, 1 gfx950, -1 other
 struct Workspace {
   void* ptr = nullptr;
   size_t bytes = 0;
+  unsigned* queue = nullptr;   // work-queue counters of the head_dim-256 prefill
 };
 std::map<std::pair<int, void*>, Workspace> g_ws;
 std::vector<std::pair<int, void*>> g_ws_retired;   // (device, pointer)
@@ -198,6 +199,30 @@ int library_workspace(int dev, hipStream_t stream, size_t need, void** ws, const
   return MIATTN_OK;
 }
 
+// The work-queue counters of (dev, stream): allocated and zeroed (by a kernel
+// on the stream, so the first launch that uses them is ordered after it) on
+// first use; every launch that uses them leaves them zero.
+int library_queue(int dev, hipStream_t stream, unsigned** q, const char* who) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  Workspace& w = g_ws[std::make_pair(dev, (void*)stream)];
+  if (w.queue == nullptr) {
+    void* p = nullptr;
+    if (hipMalloc(&p, miattn::kWorkQueueWords * sizeof(unsigned)) != hipSuccess) {
+      (void)hipGetLastError();
+      return fail(MIATTN_ERR_HIP, "%s: work-queue allocation failed", who);
+    }
+    hipLaunchKernelGGL(miattn::miattn_zero_u32_kernel, dim3(1), dim3(64), 0, stream, (unsigned*)p,
+                       miattn::kWorkQueueWords);
+    if (hipGetLastError() != hipSuccess) {
+      (void)hipFree(p);
+      return fail(MIATTN_ERR_HIP, "%s: work-queue initialisation failed", who);
+    }
+    w.queue = (unsigned*)p;
+  }
+  *q = w.queue;
+  return MIATTN_OK;
+}
+
 // Device address of `scratch` on each device (null until looked up).
 void* g_scratch_ptr[kMaxDevices];
 
@@ -323,6 +348,7 @@ void miattn_release(void) {
   }
   for (auto& kv : g_ws) {
     if (kv.second.ptr != nullptr) g_ws_retired.emplace_back(kv.first.first, kv.second.ptr);
+    if (kv.second.queue != nullptr) g_ws_retired.emplace_back(kv.first.first, (void*)kv.second.queue);
   }
   g_ws.clear();
   for (auto& r : g_ws_retired) {
@@ -406,6 +432,7 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
   a.total_tokens = total_tokens;
   a.c = c;
   a.seq_lens_k = nullptr; a.block_table = nullptr; a.max_pages = 0; a.num_pages = 0;
+  a.queue = nullptr;
   bool pp = fwd_pingpong(head_dim, false);
   // head_dim 256 (pair kernel): one query tile per work item
   long grid = fwd_setup(a, num_seqs, max_seqlen, num_q_heads, num_kv_heads, head_dim, pp, head_dim == 256);
@@ -437,14 +464,19 @@ int miattn_attn_fwd(const void* q, const void* k, const void* v, void* o, float*
       if (pp) launch_fwd_pp<128, 2, false>(a, (int)grid, cz, st);
       else launch_fwd_c<128, fwd_qb(128), 2, false, false>(a, (int)grid, cz, st);
       break;
-    default:
-      // head_dim 256: pairs of specialised waves, one query tile per
-      // workgroup
+    default: {
+      // head_dim 256: pairs of specialised waves, one query tile per work
+      // item; a persistent grid (one workgroup per compute unit) draws the
+      // `grid` items from the stream's work queues
+      const int rq = library_queue(dev, st, &a.queue, "attn_fwd");
+      if (rq) return rq;
+      const unsigned wgs = (unsigned)std::min(grid, (long)kCUs);
       if (cz)
-        hipLaunchKernelGGL((miattn::miattn_prefill_pair_kernel<true>), dim3((unsigned)grid), dim3(512), 0, st, a);
+        hipLaunchKernelGGL((miattn::miattn_prefill_pair_kernel<true>), dim3(wgs), dim3(512), 0, st, a);
       else
-        hipLaunchKernelGGL((miattn::miattn_prefill_pair_kernel<false>), dim3((unsigned)grid), dim3(512), 0, st, a);
+        hipLaunchKernelGGL((miattn::miattn_prefill_pair_kernel<false>), dim3(wgs), dim3(512), 0, st, a);
       break;
+    }
   }
   const int r = check_launch("prefill bf16");
   return r ? r : ok();
@@ -482,6 +514,7 @@ int miattn_attn_fwd_paged(const void* q, const void* k_cache, const void* v_cach
   a.c = scale * miattn::kLog2e;
   a.seq_lens_k = seq_lens_k; a.block_table = block_table;
   a.max_pages = max_pages_per_seq; a.num_pages = num_pages;
+  a.queue = nullptr;
   const long grid = fwd_setup(a, num_seqs, max_seqlen_q, num_q_heads, num_kv_heads, head_dim, false, true);
   if (grid > 0x7fffffffL) return fail(MIATTN_ERR_INVALID_ARG, "attn_fwd_paged: problem too large");
   const bool cz = causal != 0;

@@ -63,6 +63,9 @@ struct FwdArgs {
   const int32_t* block_table; // [num_seqs, max_pages]
   int max_pages;
   int num_pages;
+  // work queue of the head_dim-256 prefill: 8 per-XCD counters and an exit
+  // count, all zero when a launch starts (its last workgroup zeroes them)
+  unsigned* queue;
 };
 
 constexpr float kFwdRescaleThreshold = 8.0f;

@@ -405,7 +405,7 @@ __global__ __launch_bounds__(512, 1) void miattn_prefill_pp_kernel(FwdArgs a) {
       const int lidx = 64 * j + ln;
       const int r = lidx / CH, ch = lidx % CH;
       const u32x4 w = lds_ld16(stg + r * (2 * D) + 16 * (ch ^ osw(r)));
-      if (q0 + r < Lq) st16(a.o + ((size_t)(s0 + q0 + r) * Hq + h) * D + 8 * ch, w);
+      if (q0 + r < Lq) st16_stream(a.o + ((size_t)(s0 + q0 + r) * Hq + h) * D + 8 * ch, w);
     }
     if (qrow < Lq && a.lse != nullptr && half == 0)
       a.lse[(size_t)h * a.total_tokens + s0 + qrow] = empty ? kNegInf : (m + log2_hw(lt)) * kLn2;

@@ -40,6 +40,10 @@
  *   miattn_release. The buffer of a stream handle is reused by a later stream
  *   that gets the same handle value: destroy a stream only once the library
  *   calls enqueued on it have finished.
+ *   miattn_attn_fwd at head_dim 256 also keeps, per (device, stream), nine
+ *   32-bit work-queue counters (allocated and zeroed on the stream by the
+ *   first such call; each launch leaves them zero again), under the same
+ *   rules: no synchronisation, freed by miattn_release.
  */
 #ifndef MIATTN_H
 #define MIATTN_H

@@ -80,3 +80,43 @@ def test_streams_do_not_share_library_workspace():
     for which, (o, l) in outs:
         ref = r1 if which == 1 else r2
         assert bitwise_equal(o, ref[0]) and bitwise_equal(l, ref[1]), which
+
+
+def test_prefill_work_queues_per_stream():
+    # the head_dim-256 prefill draws its work items from counters kept per
+    # stream, which every launch leaves at zero: two problems (one with more
+    # items than compute units, one with fewer) enqueued alternately on two
+    # streams with no synchronisation between them, and back to back on one
+    # stream, must each give the bits of the call made alone
+    c1 = synth.make_prefill(31, 0, [1500, 1, 700, 0, 2100], 16, 4, 256, 2.0 ** -4, True, "bf16", "queue_a")
+    c2 = synth.make_prefill(31, 1, [40, 5], 8, 2, 256, 2.0 ** -4, True, "bf16", "queue_b")
+    d1 = (bf16_dev(c1.q), bf16_dev(c1.k), bf16_dev(c1.v), i32_dev(c1.cu_seqlens))
+    d2 = (bf16_dev(c2.q), bf16_dev(c2.k), bf16_dev(c2.v), i32_dev(c2.cu_seqlens))
+
+    def fwd(d, c):
+        return mi.attn_fwd(*d, c.max_seqlen, scale=c.scale, causal=True)
+
+    r1 = fwd(d1, c1)
+    torch.cuda.synchronize()
+    r2 = fwd(d2, c2)
+    torch.cuda.synchronize()
+    for case, (o, l) in ((c1, r1), (c2, r2)):
+        q, k, v = case.as_f64()
+        O, _ = oracle.attention_dense(q, k, v, case.cu_seqlens, case.num_q_heads, case.num_kv_heads, case.scale,
+                                      True)
+        assert_bf16_close(host(o), O, case.name)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    outs = []
+    for i in range(6):
+        with torch.cuda.stream(s1):
+            outs.append((1, fwd(d1, c1)))
+            outs.append((2, fwd(d2, c2)))
+        with torch.cuda.stream(s2):
+            outs.append((2, fwd(d2, c2)) if i % 2 else (1, fwd(d1, c1)))
+    for _ in range(3):
+        outs.append((2, fwd(d2, c2)))
+        outs.append((1, fwd(d1, c1)))
+    torch.cuda.synchronize()
+    for which, (o, l) in outs:
+        ref = r1 if which == 1 else r2
+        assert bitwise_equal(o, ref[0]) and bitwise_equal(l, ref[1]), which
