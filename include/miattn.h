@@ -44,6 +44,12 @@
  *   32-bit work-queue counters (allocated and zeroed on the stream by the
  *   first such call; each launch leaves them zero again), under the same
  *   rules: no synchronisation, freed by miattn_release.
+ *   HIP graph capture: the calls enqueue kernels only (no memset, copy or
+ *   synchronisation), so they can be captured once the capturing stream's
+ *   library-owned buffers exist: make each call once, eagerly, on that
+ *   stream before capturing (a call that would have to allocate during
+ *   capture fails). Replays and eager calls on the stream share the buffers
+ *   in stream order.
  */
 #ifndef MIATTN_H
 #define MIATTN_H
