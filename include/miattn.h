@@ -47,9 +47,9 @@
  *   HIP graph capture: the calls enqueue kernels only (no memset, copy or
  *   synchronisation), so they can be captured once the capturing stream's
  *   library-owned buffers exist: make each call once, eagerly, on that
- *   stream before capturing (a call that would have to allocate during
- *   capture fails). Replays and eager calls on the stream share the buffers
- *   in stream order.
+ *   stream before capturing, so that no call allocates device memory while
+ *   the stream is capturing. Replays and eager calls on the stream share the
+ *   buffers in stream order.
  */
 #ifndef MIATTN_H
 #define MIATTN_H
