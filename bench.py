@@ -495,6 +495,9 @@ def main():
     ap.add_argument("--sweep-splits", action="store_true",
                     help="time paged decode over split counts on a grid of batch sizes and contexts and print "
                          "the library policy's pick beside the fastest (one JSON line per cell)")
+    ap.add_argument("--graph", action="store_true",
+                    help="the step (prefill + paged decode + long decode) captured once in a HIP graph: "
+                         "time per step replayed against the same calls made eagerly on the same stream")
     ap.add_argument("--mfma-peak", action="store_true",
                     help="measure the matrix cores' sustained bf16 rate with a register-operand probe")
     ap.add_argument("--cells", action="store_true",
@@ -566,6 +569,8 @@ def main():
 
     print("[bench] generating inputs", file=sys.stderr, flush=True)
     want = {"prefill", "decode", "long", "chunked", "backward", "varlen"} if args.only is None else {args.only}
+    if args.graph:
+        want = {"prefill", "decode", "long"}
     P = Dd = Ld = None
     pc = synth.config2(S=4096, seed=0)
     if "prefill" in want or "backward" in want:
@@ -669,6 +674,38 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         print(json.dumps({"only": args.only, "ms": e0.elapsed_time(e1) / args.steps}), flush=True)
+        return
+    if args.graph:
+        # the library's per-stream buffers are made by the eager calls on the
+        # capturing stream; the graph then replays the same kernels on it
+        gs = torch.cuda.Stream()
+        with torch.cuda.stream(gs):
+            settle(stages)
+            for _ in range(args.warmup):
+                for f in stages:
+                    f()
+        gs.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gs):
+            for f in stages:
+                f()
+        res = {}
+        for mode in ("eager", "graph", "eager", "graph"):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            with torch.cuda.stream(gs):
+                e0.record(gs)
+                for _ in range(args.steps):
+                    if mode == "graph":
+                        graph.replay()
+                    else:
+                        for f in stages:
+                            f()
+                e1.record(gs)
+            gs.synchronize()
+            res[mode] = e0.elapsed_time(e1) / args.steps
+        print(json.dumps({"graph": True, "stages": "prefill S=4096 + paged decode B=64 + long decode "
+                          f"ctx={args.long_ctx}", "steps": args.steps, "eager_ms_per_step": round(res["eager"], 4),
+                          "graph_ms_per_step": round(res["graph"], 4)}), flush=True)
         return
     print(f"[bench] settle {args.settle_ms:.0f} ms, warmup {args.warmup}", file=sys.stderr, flush=True)
     settle(stages)
