@@ -140,9 +140,10 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
   const int n_tiles = (Lq + QR - 1) / QR;
   // Causal tiles i and n-1-i together cost the same for every pair, so a
   // workgroup takes such a pair. With a cached prefix at least as long as
-  // the chunk every tile costs about the same and pairing would only double
-  // the job size, so the paged grid has one unit per tile and, for such
-  // sequences, a workgroup takes one tile (units past the pairs exit).
+  // the chunk the tiles' costs differ by at most a factor of two and pairing
+  // would only double the job size, so the paged grid has one unit per tile
+  // and, for such sequences, a workgroup takes one tile, the heaviest first
+  // (units past the pairs exit).
   const bool paired = !PAGED || (CAUSAL && off < Lq);
   if (paired ? (pair > n_tiles - 1 - pair) : (pair >= n_tiles)) return;   // uniform over the workgroup
   const int n_mine = (paired && pair != n_tiles - 1 - pair) ? 2 : 1;
@@ -236,7 +237,9 @@ __global__ __launch_bounds__(256, (QB == 1 && D <= 128) ? 2 : 1) void miattn_pre
   const int bb = lane >> 4, kq = lane & 15;
 
   for (int tsel = 0; tsel < n_mine; ++tsel) {
-    const int qt = tsel == 0 ? pair : n_tiles - 1 - pair;
+    // a single tile: unit u is tile n - 1 - u, so the launch ends on light
+    // tiles
+    const int qt = !paired ? n_tiles - 1 - pair : (tsel == 0 ? pair : n_tiles - 1 - pair);
     const int q0 = qt * QR + 32 * QB * qs;   // first query row of this wave
 
     u32x4 qop[QB][NKK];
